@@ -1,0 +1,99 @@
+// Stage "unpermute_combine" (kernel_gmm_gpu.json "pieces" suite):
+//   out[t] = sum_i w[t,i] * y_sorted[inv_perm[t*k + i]] + shared_out[t]
+// as a gather-sum: one wave owns one output row, reads its k sorted expert
+// rows, accumulates in fp32 in rank order i = 0..k-1 and writes the row
+// once. No atomics, so the result is deterministic. The stage is bound by
+// HBM bandwidth: each lane moves 16-byte pieces of a row.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kCombThreads = 256;
+
+template <typename T>
+struct Vec;  // one 16-byte piece
+template <>
+struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const bf16_t* p, float* o) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    o[0] = bf16lo(v.x); o[1] = bf16hi(v.x); o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
+    o[4] = bf16lo(v.z); o[5] = bf16hi(v.z); o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
+  }
+  __device__ static void store(bf16_t* p, const float* o) {
+    uint4 v;
+    v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
+    v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+};
+template <>
+struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static void store(float* p, const float* o) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+};
+
+template <typename T, bool kShared>
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    int64_t ntok, int k, int d, const T* __restrict__ y, const float* __restrict__ w,
+    const int32_t* __restrict__ inv_perm, const T* __restrict__ shared_out, T* __restrict__ out) {
+  constexpr int N = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kCombThreads / 64) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  for (int c = lane * N; c < d; c += 64 * N) {
+    float acc[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+    for (int i = 0; i < k; ++i) {
+      const int64_t row = inv_perm[t * k + i];
+      const float wi = w[t * k + i];
+      float v[N];
+      Vec<T>::load(y + row * d + c, v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] = __builtin_fmaf(wi, v[q], acc[q]);
+    }
+    if (kShared) {
+      float v[N];
+      Vec<T>::load(shared_out + t * d + c, v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += v[q];
+    }
+    Vec<T>::store(out + t * d + c, acc);
+  }
+}
+
+template <typename T>
+hipError_t launch_combine_t(int64_t T_, int k, int d, const void* y, const float* w,
+                            const int32_t* inv, const void* sh, void* out, hipStream_t s) {
+  const int64_t blocks = (T_ + kCombThreads / 64 - 1) / (kCombThreads / 64);
+  if (sh)
+    MOE_LAUNCH("combine", (combine_kernel<T, true>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kCombThreads), 0, s, T_, k, d, static_cast<const T*>(y), w, inv,
+                       static_cast<const T*>(sh), static_cast<T*>(out));
+  else
+    MOE_LAUNCH("combine", (combine_kernel<T, false>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(kCombThreads), 0, s, T_, k, d, static_cast<const T*>(y), w, inv,
+                       static_cast<const T*>(nullptr), static_cast<T*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, int64_t T, int k, int d, const void* y_sorted,
+                          const float* topk_w, const int32_t* inv_perm, const void* shared_out,
+                          void* out, hipStream_t s) {
+  if (dtype == MOE_BF16)
+    return launch_combine_t<bf16_t>(T, k, d, y_sorted, topk_w, inv_perm, shared_out, out, s);
+  return launch_combine_t<float>(T, k, d, y_sorted, topk_w, inv_perm, shared_out, out, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,136 @@
+// Internal definitions shared by the libmoe kernels and host code (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round to nearest even; NaN inputs stay NaN (quiet bit forced).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Low / high bf16 of a packed pair, widened exactly.
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
+__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __expf(-a)); }
+
+// Elements of one storage type per 16-byte chunk.
+template <typename T>
+struct Elem;
+template <>
+struct Elem<bf16_t> {
+  static constexpr int kPer16B = 8;
+};
+template <>
+struct Elem<float> {
+  static constexpr int kPer16B = 4;
+};
+
+// Store four consecutive accumulator values as one 8-byte (bf16) or
+// 16-byte (fp32) write.
+__device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
+  uint2 v;
+  v.x = pack_bf16x2(a, b);
+  v.y = pack_bf16x2(c, d);
+  *reinterpret_cast<uint2*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void load4(const bf16_t* p, float* o) {
+  uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = bf16lo(v.x);
+  o[1] = bf16hi(v.x);
+  o[2] = bf16lo(v.y);
+  o[3] = bf16hi(v.y);
+}
+__device__ __forceinline__ void load4(const float* p, float* o) {
+  float4 v = *reinterpret_cast<const float4*>(p);
+  o[0] = v.x;
+  o[1] = v.y;
+  o[2] = v.z;
+  o[3] = v.w;
+}
+
+// XCD-aware block order: workgroups are handed to the 8 XCDs round-robin
+// (block b runs on XCD b % 8). Give each XCD one contiguous range of
+// logical work items so that neighbouring tiles (same expert, same
+// weights) share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+  const int x = b & 7, i = b >> 3;
+  const int q = nblocks >> 3, r = nblocks & 7;
+  return x * q + (x < r ? x : r) + i;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).
+void trace_push(hipStream_t s, const char* name);
+void trace_pop(hipStream_t s);
+
+#define MOE_LAUNCH(name, kernel, grid, block, lds, stream, ...)          \
+  do {                                                                  \
+    ::moe::trace_push(stream, name);                                    \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);  \
+    ::moe::trace_pop(stream);                                           \
+  } while (0)
+
+// ---------------------------------------------------------------- launches
+// Host-side launchers (defined in the .hip files). They assume validated
+// arguments and return the hipGetLastError() of their launches.
+
+hipError_t launch_route(int dtype, const void* x, const float* w_router, int64_t T, int d, int E,
+                        int k, int32_t* topk_idx, float* topk_w, hipStream_t s);
+
+size_t permute_ws_bytes(int64_t S, int E);
+hipError_t launch_permute(int64_t T, int k, int E, int bm, const int32_t* topk_idx,
+                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tiles,
+                          int32_t* num_tiles, void* ws, hipStream_t s);
+
+hipError_t launch_combine(int dtype, int64_t T, int k, int d, const void* y_sorted,
+                          const float* topk_w, const int32_t* inv_perm, const void* shared_out,
+                          void* out, hipStream_t s);
+
+struct FfnLayout {
+  // workspace offsets (bytes) of the packed weights and activations
+  size_t gu_packed, down_packed, sgu_packed, sdown_packed, h_sorted, h_shared, total;
+  // saved-buffer offsets (bytes)
+  size_t sv_ab, sv_h, sv_sab, sv_sh, sv_total;
+};
+FfnLayout ffn_layout(const moe_problem& p, bool training);
+
+hipError_t launch_ffn_fwd(const moe_problem& p, const void* x, const moe_weights& w,
+                          const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
+                          void* ws, hipStream_t s);
+
+size_t bwd_ws_bytes(const moe_problem& p);
+hipError_t launch_bwd(const moe_problem& p, const void* x, const moe_weights& w,
+                      const moe_routing& r, const void* y_sorted, const void* saved,
+                      const void* grad_out, void* grad_x, const moe_grads& g, void* ws,
+                      hipStream_t s);
+
+}  // namespace moe

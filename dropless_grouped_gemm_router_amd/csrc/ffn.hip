@@ -1,0 +1,207 @@
+// Stage "experts_grouped_swiglu" (kernel_gmm_gpu.json "pieces" suite):
+// the gated expert FFN over expert-sorted token-slots, and the shared
+// expert (gpu_moe_h100.json records, field "shared").
+//
+//   H[row]        = SiLU(x[tok] W_gate[e]) * (x[tok] W_up[e])   (gather GEMM, fused epilogue)
+//   y_sorted[row] = H[row] W_down[e]                            (grouped GEMM)
+//   shared: the same two GEMMs over all tokens, with identity row maps.
+//
+// Weights arrive in the layer's own layout ([E][d][h] and [E][h][d], N
+// contiguous) and are first packed K-contiguous for the MFMA operand
+// loads; gate and up are interleaved in 16-column groups so that one
+// 32-column MFMA tile carries matching gate and up columns and the SwiGLU
+// epilogue needs no data exchange.
+#include "gemm_core.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPackTile = 64;
+
+// dst[g][p][k] (K contiguous) from src[g][k][n] (N contiguous).
+// interleave == 0: p = n of src0. interleave != 0: dst has 2 * nsrc rows;
+// row p takes column 16 * (p / 32) + p % 16 of src0 (gate) when p % 32 < 16,
+// else the same column of src1 (up).
+template <typename T>
+__global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src0,
+                                                   const T* __restrict__ src1, T* __restrict__ dst,
+                                                   int K, int nsrc, int interleave) {
+  __shared__ T tile[kPackTile][kPackTile + 1];
+  const int ndst = interleave ? 2 * nsrc : nsrc;
+  const int p0 = blockIdx.x * kPackTile, k0 = blockIdx.y * kPackTile;
+  const int64_t gs = static_cast<int64_t>(K) * nsrc;
+  const T* s0 = src0 + blockIdx.z * gs;
+  const T* s1 = interleave ? src1 + blockIdx.z * gs : s0;
+  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
+    const int kk = i / kPackTile, pp = i % kPackTile;
+    const int pr = p0 + pp;
+    const T* s = s0;
+    int col = pr;
+    if (interleave) {
+      col = 16 * (pr / 32) + pr % 16;
+      if (pr % 32 >= 16) s = s1;
+    }
+    tile[pp][kk] = s[static_cast<int64_t>(k0 + kk) * nsrc + col];
+  }
+  __syncthreads();
+  T* d = dst + blockIdx.z * static_cast<int64_t>(ndst) * K;
+  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
+    const int pp = i / kPackTile, kk = i % kPackTile;
+    d[static_cast<int64_t>(p0 + pp) * K + k0 + kk] = tile[pp][kk];
+  }
+}
+
+template <typename T>
+void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc, bool il,
+          hipStream_t s) {
+  const int ndst = il ? 2 * nsrc : nsrc;
+  MOE_LAUNCH("pack_weights", pack_kernel<T>, dim3(ndst / kPackTile, K / kPackTile, groups), dim3(256), 0,
+                     s, static_cast<const T*>(s0), static_cast<const T*>(s1),
+                     static_cast<T*>(dst), K, nsrc, il ? 1 : 0);
+}
+
+template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
+void gemm(const char* name, const GemmArgs& a, int64_t row_tiles, hipStream_t s) {
+  if (row_tiles <= 0) return;
+  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), gemm_grid<Cfg>(row_tiles, a.N),
+             dim3(256), 0, s, a);
+}
+
+template <typename T, typename Cfg>
+void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const void* gu,
+                const void* dn, void* h_sorted, void* y_sorted, void* sa, void* sb,
+                hipStream_t s) {
+  const int64_t S = p.tokens * p.top_k;
+  const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
+  GemmArgs a{};
+  a.a = x;
+  a.lda = p.d_model;
+  a.perm = r.perm;
+  a.topk = p.top_k;
+  a.b = gu;
+  a.b_group_stride = static_cast<int64_t>(2) * p.d_hidden * p.d_model;
+  a.N = 2 * p.d_hidden;
+  a.K = p.d_model;
+  a.tiles = r.tiles;
+  a.num_tiles = r.num_tiles;
+  a.c = h_sorted;
+  a.ldc = p.d_hidden;
+  a.sa = sa;
+  a.sb = sb;
+  a.lds = 2 * static_cast<int64_t>(p.d_hidden);
+  gemm<T, Cfg, true, kEpiSwiglu, false>("gemm_gate_up", a, max_tiles, s);
+
+  GemmArgs b{};
+  b.a = h_sorted;
+  b.lda = p.d_hidden;
+  b.b = dn;
+  b.b_group_stride = static_cast<int64_t>(p.d_model) * p.d_hidden;
+  b.N = p.d_model;
+  b.K = p.d_hidden;
+  b.tiles = r.tiles;
+  b.num_tiles = r.num_tiles;
+  b.c = y_sorted;
+  b.ldc = p.d_model;
+  gemm<T, Cfg, false, kEpiStore, false>("gemm_down", b, max_tiles, s);
+}
+
+template <typename T>
+void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void* sdn, void* hs,
+                void* out, void* sa, void* sb, hipStream_t s) {
+  const int64_t row_tiles = (p.tokens + Cfg128::BM - 1) / Cfg128::BM;
+  GemmArgs a{};
+  a.a = x;
+  a.lda = p.d_model;
+  a.b = sgu;
+  a.N = 2 * p.d_shared;
+  a.K = p.d_model;
+  a.M = p.tokens;
+  a.c = hs;
+  a.ldc = p.d_shared;
+  a.sa = sa;
+  a.sb = sb;
+  a.lds = 2 * static_cast<int64_t>(p.d_shared);
+  gemm<T, Cfg128, false, kEpiSwiglu, true>("shared_gate_up", a, row_tiles, s);
+
+  GemmArgs b{};
+  b.a = hs;
+  b.lda = p.d_shared;
+  b.b = sdn;
+  b.N = p.d_model;
+  b.K = p.d_shared;
+  b.M = p.tokens;
+  b.c = out;
+  b.ldc = p.d_model;
+  gemm<T, Cfg128, false, kEpiStore, true>("shared_down", b, row_tiles, s);
+}
+
+template <typename T>
+hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
+                     const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
+                     void* ws, hipStream_t s) {
+  const FfnLayout L = ffn_layout(p, saved != nullptr);
+  char* W = static_cast<char*>(ws);
+  char* SV = static_cast<char*>(saved);
+  const int E = p.experts, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+  pack<T>(w.w_gate, w.w_up, W + L.gu_packed, E, d, h, true, s);
+  pack<T>(w.w_down, nullptr, W + L.down_packed, E, h, d, false, s);
+  if (hs > 0) {
+    pack<T>(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true, s);
+    pack<T>(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false, s);
+  }
+  T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
+  T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
+  T* sb = saved ? sa + h : nullptr;
+  switch (p.block_m) {
+    case 32:
+      routed_ffn<T, Cfg32>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
+      break;
+    case 64:
+      routed_ffn<T, Cfg64>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
+      break;
+    default:
+      routed_ffn<T, Cfg128>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
+      break;
+  }
+  if (hs > 0) {
+    T* hsb = saved ? reinterpret_cast<T*>(SV + L.sv_sh) : reinterpret_cast<T*>(W + L.h_shared);
+    T* ssa = saved ? reinterpret_cast<T*>(SV + L.sv_sab) : nullptr;
+    T* ssb = saved ? ssa + hs : nullptr;
+    shared_ffn<T>(p, x, W + L.sgu_packed, W + L.sdown_packed, hsb, shared_out, ssa, ssb, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+FfnLayout ffn_layout(const moe_problem& p, bool training) {
+  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
+  const size_t E = p.experts, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+  const size_t T = static_cast<size_t>(p.tokens), S = T * p.top_k;
+  FfnLayout L{};
+  size_t o = 0;
+  L.gu_packed = o;    o = align_up(o + E * 2 * h * d * es, 256);
+  L.down_packed = o;  o = align_up(o + E * d * h * es, 256);
+  L.sgu_packed = o;   o = align_up(o + 2 * hs * d * es, 256);
+  L.sdown_packed = o; o = align_up(o + d * hs * es, 256);
+  L.h_sorted = o;     o = align_up(o + (training ? 0 : S * h * es), 256);
+  L.h_shared = o;     o = align_up(o + (training ? 0 : T * hs * es), 256);
+  L.total = o;
+  size_t v = 0;
+  L.sv_ab = v;  v = align_up(v + S * 2 * h * es, 256);
+  L.sv_h = v;   v = align_up(v + S * h * es, 256);
+  L.sv_sab = v; v = align_up(v + T * 2 * hs * es, 256);
+  L.sv_sh = v;  v = align_up(v + T * hs * es, 256);
+  L.sv_total = v;
+  return L;
+}
+
+hipError_t launch_ffn_fwd(const moe_problem& p, const void* x, const moe_weights& w,
+                          const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
+                          void* ws, hipStream_t s) {
+  if (p.dtype == MOE_BF16) return ffn_fwd_t<bf16_t>(p, x, w, r, y_sorted, shared_out, saved, ws, s);
+  return ffn_fwd_t<float>(p, x, w, r, y_sorted, shared_out, saved, ws, s);
+}
+
+}  // namespace moe

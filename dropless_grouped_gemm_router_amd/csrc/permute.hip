@@ -1,0 +1,209 @@
+// Stage "sort_permute" (kernel_gmm_gpu.json "pieces" suite): a stable
+// counting sort of the T*k flat token-slots by expert, and the block_m tile
+// schedule of the grouped GEMM.
+//
+//   1. count:   each block of kSlotsPerBlock consecutive flat slots counts
+//               its slots per expert (integer LDS atomics: order-free sums).
+//   2. scan:    one workgroup scans the [expert][block] counts (expert-
+//               major, block-minor), which yields every block's first row per
+//               expert and the expert offsets, then writes the tile list.
+//   3. scatter: each block ranks its slots within each expert in flat order
+//               (wave ballots give the rank among equal experts in a
+//               64-slot step; running per-expert counters carry it across
+//               steps and waves) and writes perm / inv_perm.
+// The result is unique (stable by flat slot), so it matches a sequential
+// counting sort bit for bit. No device-to-host synchronisation: the tile
+// count stays on the device and the GEMMs are sized on the host by the
+// upper bound ceil(S / block_m) + E.
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPermThreads = 256;
+constexpr int kSlotsPerWave = 1024;
+constexpr int kSlotsPerBlock = kSlotsPerWave * (kPermThreads / 64);  // 4096
+constexpr int kMaxE = 64;
+
+__global__ __launch_bounds__(kPermThreads) void count_kernel(const int32_t* __restrict__ idx,
+                                                             int64_t S, int E, int nblk,
+                                                             int32_t* __restrict__ blk_counts) {
+  __shared__ int32_t c[kMaxE];
+  for (int e = threadIdx.x; e < E; e += kPermThreads) c[e] = 0;
+  __syncthreads();
+  const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kSlotsPerBlock;
+  for (int i = threadIdx.x; i < kSlotsPerBlock; i += kPermThreads) {
+    const int64_t s = s0 + i;
+    if (s < S) atomicAdd(&c[idx[s]], 1);
+  }
+  __syncthreads();
+  // Expert-major layout [E][nblk]: a flat exclusive scan of it is, for
+  // every (expert, block), the expert's offset plus the rows of that expert
+  // in earlier blocks.
+  for (int e = threadIdx.x; e < E; e += kPermThreads)
+    blk_counts[static_cast<int64_t>(e) * nblk + blockIdx.x] = c[e];
+}
+
+constexpr int kScanThreads = 1024;
+
+// One workgroup: in-place exclusive scan of blk_counts[E * nblk], then the
+// expert offsets and the tile list.
+__global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ blk_counts,
+                                                            int nblk, int E, int bm, int64_t S,
+                                                            int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ tiles,
+                                                            int32_t* __restrict__ num_tiles) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  __shared__ int32_t off[kMaxE + 1];
+  __shared__ int32_t tile_off[kMaxE + 1];
+  const int64_t L = static_cast<int64_t>(E) * nblk;
+  const int64_t chunk = (L + kScanThreads - 1) / kScanThreads;
+  const int64_t b0 = min(L, chunk * threadIdx.x), b1 = min(L, b0 + chunk);
+  int32_t local = 0;
+  for (int64_t i = b0; i < b1; ++i) local += blk_counts[i];
+  // Exclusive scan of the per-thread sums: within the wave, then across waves.
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t incl = local;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t run = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int32_t v = wsum[w];
+      wsum[w] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int32_t run = wsum[wave] + incl - local;
+  for (int64_t i = b0; i < b1; ++i) {
+    const int32_t v = blk_counts[i];
+    blk_counts[i] = run;
+    if (i % nblk == 0) off[i / nblk] = run;  // block 0 of expert i / nblk
+    run += v;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    off[E] = static_cast<int32_t>(S);
+    int32_t nt = 0;
+    for (int e = 0; e < E; ++e) {
+      tile_off[e] = nt;
+      nt += (off[e + 1] - off[e] + bm - 1) / bm;
+    }
+    tile_off[E] = nt;
+    *num_tiles = nt;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e <= E; e += kScanThreads) offsets[e] = off[e];
+  // Tile n of expert e covers rows [off[e] + (n - tile_off[e]) * bm, ...),
+  // at most bm of them.
+  const int32_t nt = tile_off[E];
+  for (int32_t n = threadIdx.x; n < nt; n += kScanThreads) {
+    int lo = 0, hi = E - 1;  // last e with tile_off[e] <= n
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_off[mid] <= n) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int32_t r = (n - tile_off[e]) * bm;
+    tiles[3 * n + 0] = e;
+    tiles[3 * n + 1] = off[e] + r;
+    tiles[3 * n + 2] = min(bm, off[e + 1] - off[e] - r);
+  }
+}
+
+// Lanes of this wave whose expert equals mine (E <= 64: six ballots on the
+// bits of the expert index; lanes past the end carry the value E).
+__device__ __forceinline__ uint64_t same_expert_mask(int e) {
+  uint64_t m = ~0ull;
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const uint64_t bal = __ballot((e >> b) & 1);
+    m &= ((e >> b) & 1) ? bal : ~bal;
+  }
+  return m;
+}
+
+__global__ __launch_bounds__(kPermThreads) void scatter_kernel(const int32_t* __restrict__ idx,
+                                                               int64_t S, int E, int nblk,
+                                                               const int32_t* __restrict__ blk_base,
+                                                               int32_t* __restrict__ perm,
+                                                               int32_t* __restrict__ inv_perm) {
+  __shared__ int32_t wave_cnt[kPermThreads / 64][kMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < (kPermThreads / 64) * kMaxE; i += kPermThreads)
+    (&wave_cnt[0][0])[i] = 0;
+  __syncthreads();
+  const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kSlotsPerBlock +
+                     static_cast<int64_t>(wave) * kSlotsPerWave;
+  // Pass 1: per-wave counts.
+  for (int i = lane; i < kSlotsPerWave; i += 64) {
+    const int64_t s = w0 + i;
+    if (s < S) atomicAdd(&wave_cnt[wave][idx[s]], 1);
+  }
+  __syncthreads();
+  // Per-wave running counters start at the block base plus the counts of
+  // the earlier waves of the block.
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    int32_t run = blk_base[static_cast<int64_t>(e) * nblk + blockIdx.x];
+    for (int w = 0; w < kPermThreads / 64; ++w) {
+      const int32_t c = wave_cnt[w][e];
+      wave_cnt[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  // Pass 2: stable ranks, 64 slots per step in flat order.
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = 0; i0 < kSlotsPerWave; i0 += 64) {
+    const int64_t s = w0 + i0 + lane;
+    const bool ok = s < S;
+    const int e = ok ? idx[s] : E;
+    const uint64_t m = same_expert_mask(e);
+    const int rank = __popcll(m & lt);
+    const int cnt = __popcll(m);
+    if (ok) {
+      const int32_t base = wave_cnt[wave][e];
+      const int32_t pos = base + rank;
+      perm[pos] = static_cast<int32_t>(s);
+      inv_perm[s] = pos;
+    }
+    // All lanes have read their base (the read above precedes this point
+    // in the wave's in-order LDS queue); the last lane of each expert group
+    // advances its counter.
+    __builtin_amdgcn_wave_barrier();
+    if (ok && rank == cnt - 1) wave_cnt[wave][e] += cnt;
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int64_t S, int E) {
+  const int64_t nblk = (S + kSlotsPerBlock - 1) / kSlotsPerBlock;
+  return align_up(sizeof(int32_t) * static_cast<size_t>(nblk) * E, 256);
+}
+
+hipError_t launch_permute(int64_t T, int k, int E, int bm, const int32_t* topk_idx,
+                          int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tiles,
+                          int32_t* num_tiles, void* ws, hipStream_t s) {
+  const int64_t S = T * k;
+  const int nblk = static_cast<int>((S + kSlotsPerBlock - 1) / kSlotsPerBlock);
+  int32_t* blk = static_cast<int32_t*>(ws);
+  MOE_LAUNCH("permute_count", count_kernel, dim3(nblk), dim3(kPermThreads), 0, s, topk_idx, S, E, nblk,
+                     blk);
+  MOE_LAUNCH("permute_scan", scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, nblk, E, bm, S, offsets,
+                     tiles, num_tiles);
+  MOE_LAUNCH("permute_scatter", scatter_kernel, dim3(nblk), dim3(kPermThreads), 0, s, topk_idx, S, E, nblk,
+                     blk, perm, inv_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,180 @@
+"""libmoe on the host, no GPU: the library loads and exports every symbol
+include/moe.h declares, host-side helpers, and every argument check, all of
+which run before any HIP call."""
+
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+from dropless_grouped_gemm_router_amd import binding as B
+from dropless_grouped_gemm_router_amd.inputs import Problem, WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = B.load()
+    names = declared_functions()
+    assert len(names) == 14
+    assert sorted(B.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "gfx950" in B.moe_version()
+
+
+def test_param_count_and_tiles():
+    p = Problem(4096, 8, 2, 512, 1024, 0, "fp32", 64)
+    assert B.moe_param_count(p) == 12587008  # gpu_nn.json, moe suite, "params"
+    assert B.moe_max_tiles(p) == 8192 // 64 + 8
+    p3 = WORKLOADS[3][1]
+    assert B.moe_param_count(p3) == 3 * 64 * 512 * 128 + 512 * 64 + 3 * 512 * 1024
+    assert B.moe_max_tiles(p3) == 131072 * 8 // 128 + 64
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(experts=0), B.MOE_ERR_INVALID),
+    (dict(top_k=0), B.MOE_ERR_INVALID),
+    (dict(top_k=9), B.MOE_ERR_INVALID),
+    (dict(tokens=-1), B.MOE_ERR_INVALID),
+    (dict(dtype=7), B.MOE_ERR_INVALID),
+    (dict(d_shared=-64), B.MOE_ERR_INVALID),
+    (dict(experts=65, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(block_m=48), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=500), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_hidden=100), B.MOE_ERR_UNSUPPORTED),
+    (dict(d_shared=96), B.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=1 << 30, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(), B.MOE_OK),
+    (dict(tokens=0), B.MOE_OK),
+])
+def test_check_problem(kw, code):
+    base = dict(tokens=10, experts=8, top_k=2, d_model=256, d_hidden=128, d_shared=0,
+                dtype=B.MOE_BF16, block_m=64)
+    base.update(kw)
+    p = B.moe_problem(**base)
+    assert B.load().moe_check_problem(ctypes.byref(p)) == code
+    if code != B.MOE_OK:
+        assert B.load().moe_workspace_bytes(ctypes.byref(p), 1) == 0
+        assert B.load().moe_max_tiles(ctypes.byref(p)) == 0
+        assert B.load().moe_param_count(ctypes.byref(p)) == -1
+
+
+class FakeTensor:
+    """Host stand-in with an arbitrary (never dereferenced) address."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def fake_routing(base=0x10000000):
+    return {n: FakeTensor(base + i * 0x100000) for i, n in enumerate(
+        ["topk_idx", "topk_w", "expert_offsets", "perm", "inv_perm", "tiles", "num_tiles"])}
+
+
+def fake_weights(base=0x20000000, shared=True):
+    names = ["w_router", "w_gate", "w_up", "w_down"] + (["ws_gate", "ws_up", "ws_down"] if shared else [])
+    return {n: FakeTensor(base + i * 0x100000) for i, n in enumerate(names)}
+
+
+P = Problem(100, 8, 2, 256, 128, 64, "bf16", 64)
+
+
+def expect(code, fn, *a, **k):
+    with pytest.raises(B.MoeError) as e:
+        fn(*a, **k)
+    assert e.value.status == code
+
+
+def test_route_argument_errors():
+    r = fake_routing()
+    expect(B.MOE_ERR_INVALID, B.moe_route, P, None, FakeTensor(0x3000), r, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_route, P, FakeTensor(0x3008), FakeTensor(0x3000), r, stream=0)
+    r2 = dict(r, topk_idx=None)
+    expect(B.MOE_ERR_INVALID, B.moe_route, P, FakeTensor(0x3000), FakeTensor(0x3000), r2, stream=0)
+    bad = Problem(100, 8, 9, 256, 128, 0, "bf16", 64)
+    expect(B.MOE_ERR_INVALID, B.moe_route, bad, FakeTensor(0x3000), FakeTensor(0x3000), r, stream=0)
+    # zero tokens: a successful no-op, pointers unused
+    B.moe_route(Problem(0, 8, 2, 256, 128, 0, "bf16", 64), None, None, {}, stream=0)
+
+
+def test_permute_argument_errors():
+    r = fake_routing()
+    need = B.moe_workspace_bytes(P)
+    ws = FakeTensor(0x40000000)
+    expect(B.MOE_ERR_WORKSPACE, B.moe_permute, P, r, ws, workspace_bytes=0, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_permute, P, r, FakeTensor(0x40000010), workspace_bytes=need,
+           stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_permute, P, dict(r, perm=None), ws, workspace_bytes=need,
+           stream=0)
+    B.moe_permute(Problem(0, 8, 2, 256, 128, 0, "bf16", 64), {}, None, workspace_bytes=0, stream=0)
+
+
+def test_ffn_and_combine_argument_errors():
+    r, w = fake_routing(), fake_weights()
+    ws = FakeTensor(0x40000000)
+    need = B.moe_workspace_bytes(P)
+    y, sh, out = FakeTensor(0x50000000), FakeTensor(0x51000000), FakeTensor(0x52000000)
+    x = FakeTensor(0x53000000)
+    expect(B.MOE_ERR_WORKSPACE, B.moe_ffn_fwd, P, x, w, r, y, sh, None, ws, workspace_bytes=need - 1,
+           stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_ffn_fwd, P, x, fake_weights(shared=False), r, y, sh, None, ws,
+           workspace_bytes=need, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_ffn_fwd, P, x, w, r, y, None, None, ws, workspace_bytes=need,
+           stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_ffn_fwd, P, x, w, r, y, sh, FakeTensor(0x60000010), ws,
+           workspace_bytes=need, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_combine, P, y, dict(r, inv_perm=None), sh, out, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_combine, P, y, r, FakeTensor(0x51000004), out, stream=0)
+
+
+def test_bwd_argument_errors():
+    r, w = fake_routing(), fake_weights()
+    g = {n: FakeTensor(0x70000000 + i * 0x100000) for i, n in
+         enumerate(["w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"])}
+    a = [FakeTensor(0x50000000), FakeTensor(0x54000000), FakeTensor(0x55000000),
+         FakeTensor(0x56000000)]
+    x = FakeTensor(0x53000000)
+    ws = FakeTensor(0x40000000)
+    need = B.moe_workspace_bytes(P, training=True)
+    expect(B.MOE_ERR_INVALID, B.moe_bwd, P, x, w, r, a[0], a[1], a[2], a[3], dict(g, ws_up=None),
+           ws, workspace_bytes=need, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_bwd, P, x, w, r, a[0], None, a[2], a[3], g, ws,
+           workspace_bytes=need, stream=0)
+    if need > B.moe_workspace_bytes(P, training=False):
+        expect(B.MOE_ERR_WORKSPACE, B.moe_bwd, P, x, w, r, a[0], a[1], a[2], a[3], g, ws,
+               workspace_bytes=need - 1, stream=0)
+
+
+def test_buffer_layouts_match_pages_argument_bytes():
+    """The stage inputs have the byte sizes the pages' 'pieces' records
+    report: storage-dtype tokens with an fp32 router, storage-dtype sorted
+    rows [T*k, d] and weights, fp32 combine weights."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_arg_bytes.json")))
+    for c in g["cases"]:
+        dt = "fp32" if c["dtype"] == "float32" else "bf16"
+        p = Problem(c["tokens"], 8, 2, 512, 1024, 0, dt, 64)
+        b = B.allocate(p, device="cpu")
+        es = 4 if dt == "fp32" else 2
+        x_bytes = p.tokens * p.d_model * es
+        w_bytes = 3 * p.experts * p.d_model * p.d_hidden * es
+        if c["piece"] == "route":
+            got = x_bytes + p.d_model * p.experts * 4  # w_router is fp32
+        elif c["piece"] == "experts_grouped_swiglu":
+            got = b.y_sorted.numel() * b.y_sorted.element_size() + w_bytes
+        else:
+            got = (b.y_sorted.numel() * b.y_sorted.element_size()
+                   + b.routing["topk_w"].numel() * b.routing["topk_w"].element_size())
+        assert got == int(round(c["xla_arg_mb"] * 2 ** 20)), c

@@ -1,0 +1,125 @@
+"""HIP forward path vs the oracle, through the C ABI (GPU)."""
+
+import numpy as np
+import pytest
+
+from dropless_grouped_gemm_router_amd.inputs import Problem, WORKLOADS
+from oracle import oracle
+
+from gpu_util import TOL, Case, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def check_routing(c: Case, nthreads=0):
+    """Routing ints bit-exact; weights to fp32 rounding."""
+    p, v = c.p, c.v
+    _, idx, w = oracle.route(v["x"], v["w_router"], p.top_k, nthreads)
+    g = c.routing_np()
+    assert np.array_equal(g["topk_idx"], idx)
+    assert np.max(np.abs(g["topk_w"] - w)) < 2e-6
+    r = oracle.permute(idx, p.experts, p.block_m)
+    assert np.array_equal(g["offsets"], r["offsets"])
+    assert np.array_equal(g["perm"], r["perm"])
+    assert np.array_equal(g["inv_perm"], r["inv_perm"])
+    assert g["num_tiles"] == r["num_tiles"]
+    assert np.array_equal(g["tiles"], r["tiles"])
+    return idx, w, r
+
+
+SMALL = [
+    # tokens, E, k, d, h, hs, dtype, bm  -- several tiles and ragged tails
+    Problem(300, 8, 2, 256, 128, 0, "bf16", 64),
+    Problem(300, 8, 2, 256, 128, 0, "fp32", 64),
+    Problem(517, 16, 4, 256, 192, 128, "bf16", 128),
+    Problem(517, 16, 4, 256, 192, 128, "fp32", 32),
+    Problem(1, 4, 2, 128, 64, 64, "bf16", 32),
+    Problem(97, 1, 1, 128, 64, 0, "bf16", 128),
+    Problem(200, 5, 5, 128, 64, 0, "fp32", 64),
+    Problem(1000, 64, 8, 128, 64, 64, "bf16", 128),
+]
+
+
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}")
+def test_forward_small_elementwise(p):
+    note(f"forward small {p}")
+    c = Case(p, seed=7)
+    out = c.forward()
+    idx, w, r = check_routing(c)
+    ref, y = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx, w,
+                                 *c.shared(), want_y=True)
+    ys = to_np(c.buf.y_sorted)
+    # sorted expert outputs: row inv_perm[s] holds the unweighted output of flat slot s
+    assert oracle.rel_err(ys[r["inv_perm"]], y) < TOL[p.dtype]
+    if p.d_shared:
+        sref = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx,
+                                   np.zeros_like(w), *c.shared())
+        assert oracle.rel_err(to_np(c.buf.shared_out), sref) < TOL[p.dtype]
+    assert oracle.rel_err(to_np(out), ref) < TOL[p.dtype]
+    assert np.all(np.isfinite(to_np(out)))
+
+
+def test_forward_deterministic():
+    p = Problem(777, 8, 2, 256, 128, 128, "bf16", 64)
+    c = Case(p, seed=3)
+    a = c.forward().clone()
+    ya = c.buf.y_sorted.clone()
+    b = c.forward()
+    assert bool((a.view(-1).view(dtype=__import__("torch").int16) ==
+                 b.view(-1).view(dtype=__import__("torch").int16)).all())
+    assert bool((ya == c.buf.y_sorted).all())
+
+
+def test_skewed_routing_empty_experts():
+    """A router that sends every token to experts 0 and 1: two experts with
+    every slot (many tiles each), the rest empty."""
+    import torch
+    p = Problem(700, 8, 2, 128, 64, 0, "bf16", 32)
+    c = Case(p, seed=5)
+    wr = np.zeros((128, 8), np.float32)
+    wr[:, 0] = 1.0
+    wr[:, 1] = 0.5
+    c.inputs["w_router"].stored = wr
+    c.inputs["w_router"].value = wr
+    c.v["w_router"] = wr
+    c.dev["w_router"] = torch.from_numpy(wr).cuda()
+    # make x positive so experts 0, 1 always lead
+    xs = np.abs(c.v["x"]).astype(np.float32)
+    from dropless_grouped_gemm_router_amd.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+    bits = f32_to_bf16_bits(xs)
+    c.v["x"] = bf16_bits_to_f32(bits).reshape(xs.shape)
+    c.dev["x"] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    out = c.forward()
+    idx, w, r = check_routing(c)
+    assert np.all(idx[:, 0] == 0) and np.all(idx[:, 1] == 1)
+    assert r["num_tiles"] == 2 * ((700 + 31) // 32)
+    ref = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx, w)
+    assert oracle.rel_err(to_np(out), ref) < TOL["bf16"]
+
+
+def test_zero_tokens_is_noop():
+    import torch
+    from dropless_grouped_gemm_router_amd import binding as B
+    p = Problem(0, 8, 2, 256, 128, 0, "bf16", 64)
+    B.moe_route(p, None, None, {})
+    B.moe_permute(p, {}, None, workspace_bytes=0)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_workload_full_size_sampled(cfg):
+    """The measured workloads at full size: routing and permutation bit-exact
+    on every token, outputs on a sample of rows."""
+    name, p, _ = WORKLOADS[cfg]
+    note(f"workload {cfg}: {name}")
+    c = Case(p, seed=0)
+    out = c.forward()
+    idx, w, r = check_routing(c, nthreads=0)
+    rng = np.random.default_rng(cfg)
+    rows = np.unique(np.concatenate([[0, p.tokens - 1], rng.choice(p.tokens, 254, replace=False)]))
+    ref = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx, w,
+                              *c.shared(), rows=rows)
+    got = to_np(out[rows.tolist()])
+    err = oracle.rel_err(got, ref)
+    note(f"workload {cfg}: out rel err {err:.3e}")
+    assert err < TOL[p.dtype]
