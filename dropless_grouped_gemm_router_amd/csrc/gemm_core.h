@@ -91,6 +91,48 @@ struct Mfma<float> {
   }
 };
 
+// Pipeline pieces of the GEMM main loop (force-inlined so that the staging
+// registers stay in VGPRs).
+template <int A_CH, int B_CH>
+__device__ __forceinline__ void gemm_gload(uint4 (&ra)[A_CH], uint4 (&rb)[B_CH],
+                                           const char* const (&a_src)[A_CH], const char* b_base,
+                                           const int (&b_off)[B_CH], int off) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_base + b_off[i] + off);
+}
+
+template <int A_CH, int B_CH>
+__device__ __forceinline__ void gemm_lstore(char* s, const uint4 (&ra)[A_CH],
+                                            const uint4 (&rb)[B_CH], const int (&a_dst)[A_CH],
+                                            const int (&b_dst)[B_CH]) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(s + a_dst[i]) = ra[i];
+#pragma unroll
+  for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(s + b_dst[i]) = rb[i];
+}
+
+// One K stage out of LDS: four fragment steps of 32 bytes per row.
+template <typename T, int WM_SUB, int WN_SUB>
+__device__ __forceinline__ void gemm_compute(const char* s, int a_frag, int b_frag,
+                                             f32x16_t (&acc)[WM_SUB][WN_SUB]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint4 xf[WM_SUB], wf[WN_SUB];
+#pragma unroll
+    for (int i = 0; i < WM_SUB; ++i)
+      xf[i] = *reinterpret_cast<const uint4*>(s + a_frag + i * 32 * kLdsRowBytes + q * 32);
+#pragma unroll
+    for (int j = 0; j < WN_SUB; ++j)
+      wf[j] = *reinterpret_cast<const uint4*>(s + b_frag + j * 32 * kLdsRowBytes + q * 32);
+#pragma unroll
+    for (int i = 0; i < WM_SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < WN_SUB; ++j) Mfma<T>::step(wf[j], xf[i], acc[i][j]);
+  }
+}
+
 template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs p) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN;
@@ -165,50 +207,24 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  uint4 ra[A_CH], rb[B_CH];
-  auto gload = [&](int ks) {
-    const int off = ks * kStageBytes;
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
-    const char* bb = ks < ks_split ? b_base : b2_base;
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(bb + b_off[i] + off);
-  };
-  auto lstore = [&](int buf) {
-    char* s = smem + buf * (A_BYTES + B_BYTES);
-#pragma unroll
-    for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(s + a_dst[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(s + b_dst[i]) = rb[i];
-  };
-
   const int nk = p.K / KT;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int a_frag = (wm * WM_SUB * 32 + r32) * kLdsRowBytes + g * 16;
   const int b_frag = A_BYTES + (wn * WN_SUB * 32 + r32) * kLdsRowBytes + g * 16;
-  for (int ks = 0; ks < nk; ++ks) {
+  uint4 ra[A_CH], rb[B_CH];
+  gemm_gload<A_CH, B_CH>(ra, rb, a_src, b_base, b_off, 0);
+  gemm_lstore<A_CH, B_CH>(smem, ra, rb, a_dst, b_dst);
+  __syncthreads();
+  // Software pipeline: stage ks+1 is fetched into registers while stage ks
+  // is multiplied out of LDS; the last stage is peeled.
+  for (int ks = 0; ks + 1 < nk; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
-    const char* s = smem + buf * (A_BYTES + B_BYTES);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 xf[WM_SUB], wf[WN_SUB];
-#pragma unroll
-      for (int i = 0; i < WM_SUB; ++i)
-        xf[i] = *reinterpret_cast<const uint4*>(s + a_frag + i * 32 * kLdsRowBytes + q * 32);
-#pragma unroll
-      for (int j = 0; j < WN_SUB; ++j)
-        wf[j] = *reinterpret_cast<const uint4*>(s + b_frag + j * 32 * kLdsRowBytes + q * 32);
-#pragma unroll
-      for (int i = 0; i < WM_SUB; ++i)
-#pragma unroll
-        for (int j = 0; j < WN_SUB; ++j) Mfma<T>::step(wf[j], xf[i], acc[i][j]);
-    }
-    if (ks + 1 < nk) lstore(buf ^ 1);
+    gemm_gload<A_CH, B_CH>(ra, rb, a_src, ks + 1 < ks_split ? b_base : b2_base, b_off,
+                           (ks + 1) * kStageBytes);
+    gemm_compute<T, WM_SUB, WN_SUB>(smem + buf * (A_BYTES + B_BYTES), a_frag, b_frag, acc);
+    gemm_lstore<A_CH, B_CH>(smem + (buf ^ 1) * (A_BYTES + B_BYTES), ra, rb, a_dst, b_dst);
     __syncthreads();
   }
+  gemm_compute<T, WM_SUB, WN_SUB>(smem + ((nk - 1) & 1) * (A_BYTES + B_BYTES), a_frag, b_frag, acc);
 
   // Epilogue. Accumulator register q of MFMA tile (i, j) holds row
   // m = i*32 + r32 and column n = j*32 + 8*(q/4) + 4*g + q%4 of the wave's
@@ -337,6 +353,56 @@ struct Transpose<float> {
   }
 };
 
+// Stage loader of the weight-gradient kernel: thread `tid` fetches its
+// V x V blocks of A (blocks 0 .. NB-1) and B (NB .. 2NB-1); rows outside
+// [r0, r1) read as zeros.
+template <typename T, bool kGatherA, int PER, int V, int NB, int KT>
+__device__ __forceinline__ void wgrad_gload(const WgradArgs& p, uint4 (&blk)[PER][V], int64_t r0,
+                                            int64_t r1, int ks, int mt, int nt, int tid) {
+  constexpr int CB = 128 / V;  // column blocks per operand row
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = tid + q * 256;
+    const bool is_b = b >= NB;
+    const int bb = is_b ? b - NB : b;
+    const int rb = bb / CB, cb = bb % CB;
+#pragma unroll
+    for (int rr = 0; rr < V; ++rr) {
+      const int64_t r = r0 + static_cast<int64_t>(ks) * KT + rb * V + rr;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < r1) {
+        const T* src;
+        if (is_b) {
+          src = static_cast<const T*>(p.b) + r * p.ldb + nt * 128 + cb * V;
+        } else {
+          const int64_t ar = kGatherA ? static_cast<int64_t>(p.perm[r] / p.topk) : r;
+          src = static_cast<const T*>(p.a) + ar * p.lda + mt * 128 + cb * V;
+        }
+        v = *reinterpret_cast<const uint4*>(src);
+      }
+      blk[q][rr] = v;
+    }
+  }
+}
+
+// Transposes the fetched blocks into K-contiguous LDS rows.
+template <typename T, int PER, int V, int NB, int A_BYTES>
+__device__ __forceinline__ void wgrad_lstore(char* s, const uint4 (&blk)[PER][V], int tid) {
+  constexpr int CB = 128 / V;
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int b = tid + q * 256;
+    const bool is_b = b >= NB;
+    const int bb = is_b ? b - NB : b;
+    const int rb = bb / CB, cb = bb % CB;
+    uint4 t[V];
+    Transpose<T>::run(blk[q], t);
+    char* base = s + (is_b ? A_BYTES : 0) + rb * 16;
+#pragma unroll
+    for (int cc = 0; cc < V; ++cc) *reinterpret_cast<uint4*>(base + (cb * V + cc) * kLdsRowBytes) = t[cc];
+  }
+}
+
 template <typename T, bool kGatherA, bool kDense>
 __global__ __launch_bounds__(256, 2) void wgrad_kernel(const WgradArgs p) {
   constexpr int BM = 128, BN = 128, WM_SUB = 2, WN_SUB = 2;
@@ -365,49 +431,6 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const WgradArgs p) {
   const int g = lane >> 5, r32 = lane & 31;
   const int wm = wave >> 1, wn = wave & 1;
 
-  uint4 blk[PER][V];
-  auto gload = [&](int ks) {
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int b = tid + q * 256;
-      const bool is_b = b >= NB;
-      const int bb = is_b ? b - NB : b;
-      const int rb = bb / (BM / V), cb = bb % (BM / V);
-#pragma unroll
-      for (int rr = 0; rr < V; ++rr) {
-        const int64_t r = r0 + static_cast<int64_t>(ks) * KT + rb * V + rr;
-        if (r < r1) {
-          const T* src;
-          if (is_b) {
-            src = static_cast<const T*>(p.b) + r * p.ldb + nt * BN + cb * V;
-          } else {
-            const int64_t ar = kGatherA ? static_cast<int64_t>(p.perm[r] / p.topk) : r;
-            src = static_cast<const T*>(p.a) + ar * p.lda + mt * BM + cb * V;
-          }
-          blk[q][rr] = *reinterpret_cast<const uint4*>(src);
-        } else {
-          blk[q][rr] = make_uint4(0u, 0u, 0u, 0u);
-        }
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    char* s = smem + buf * (A_BYTES + B_BYTES);
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      const int b = tid + q * 256;
-      const bool is_b = b >= NB;
-      const int bb = is_b ? b - NB : b;
-      const int rb = bb / (BM / V), cb = bb % (BM / V);
-      uint4 t[V];
-      Transpose<T>::run(blk[q], t);
-      char* base = s + (is_b ? A_BYTES : 0) + rb * 16;
-#pragma unroll
-      for (int cc = 0; cc < V; ++cc)
-        *reinterpret_cast<uint4*>(base + (cb * V + cc) * kLdsRowBytes) = t[cc];
-    }
-  };
-
   f32x16_t acc[WM_SUB][WN_SUB];
 #pragma unroll
   for (int i = 0; i < WM_SUB; ++i)
@@ -419,31 +442,20 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const WgradArgs p) {
   const int nk = static_cast<int>((r1 - r0 + KT - 1) / KT);
   const int a_frag = (wm * WM_SUB * 32 + r32) * kLdsRowBytes + g * 16;
   const int b_frag = A_BYTES + (wn * WN_SUB * 32 + r32) * kLdsRowBytes + g * 16;
+  uint4 blk[PER][V];
   if (nk > 0) {
-    gload(0);
-    lstore(0);
+    wgrad_gload<T, kGatherA, PER, V, NB, KT>(p, blk, r0, r1, 0, mt, nt, tid);
+    wgrad_lstore<T, PER, V, NB, A_BYTES>(smem, blk, tid);
     __syncthreads();
-  }
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nk) gload(ks + 1);
-    const char* s = smem + buf * (A_BYTES + B_BYTES);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint4 xf[WM_SUB], wf[WN_SUB];
-#pragma unroll
-      for (int i = 0; i < WM_SUB; ++i)
-        xf[i] = *reinterpret_cast<const uint4*>(s + a_frag + i * 32 * kLdsRowBytes + q * 32);
-#pragma unroll
-      for (int j = 0; j < WN_SUB; ++j)
-        wf[j] = *reinterpret_cast<const uint4*>(s + b_frag + j * 32 * kLdsRowBytes + q * 32);
-#pragma unroll
-      for (int i = 0; i < WM_SUB; ++i)
-#pragma unroll
-        for (int j = 0; j < WN_SUB; ++j) Mfma<T>::step(wf[j], xf[i], acc[i][j]);
+    for (int ks = 0; ks + 1 < nk; ++ks) {
+      const int buf = ks & 1;
+      wgrad_gload<T, kGatherA, PER, V, NB, KT>(p, blk, r0, r1, ks + 1, mt, nt, tid);
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + buf * (A_BYTES + B_BYTES), a_frag, b_frag, acc);
+      wgrad_lstore<T, PER, V, NB, A_BYTES>(smem + (buf ^ 1) * (A_BYTES + B_BYTES), blk, tid);
+      __syncthreads();
     }
-    if (ks + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
+    gemm_compute<T, WM_SUB, WN_SUB>(smem + ((nk - 1) & 1) * (A_BYTES + B_BYTES), a_frag, b_frag,
+                                    acc);
   }
 
   float* cg = p.c + grp * p.c_group_stride;

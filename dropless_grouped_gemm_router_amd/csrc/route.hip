@@ -18,7 +18,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kRouteChunk = 256;  // router rows (j) staged in LDS per pass
+constexpr int kRouteChunk = 128;  // router rows (j) staged in LDS per pass
 constexpr int kRoutePad = 4;      // LDS row padding (floats): conflict-free 16-byte reads
 
 __device__ __forceinline__ void load8(const bf16_t* p, float* o) {
@@ -42,17 +42,23 @@ __device__ __forceinline__ bool ranks_before(float av, int ae, float bv, int be)
   return (av > bv) || (av == bv && ae < be);
 }
 
-template <typename T, int EP, int R>
+// Lane layout: a token group of L lanes covers one token's experts, lane
+// le of the group owning experts le, le + L, ..., le + (P-1) L; each lane
+// evaluates R tokens for each of its P experts, so every token value read
+// (and widened) feeds P multiply-adds and every router value read from LDS
+// feeds R. 64 / L token groups per wave.
+template <typename T, int L, int P, int R>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const T* __restrict__ x,
                                                               const float* __restrict__ wr,
                                                               int64_t ntok, int d, int E, int k,
                                                               int32_t* __restrict__ topk_idx,
                                                               float* __restrict__ topk_w) {
-  __shared__ __attribute__((aligned(16))) float w_lds[EP * (kRouteChunk + kRoutePad)];  // [e][j]
-  constexpr int kGroups = 64 / EP;  // token groups per wave
+  constexpr int EPAD = L * P;
+  __shared__ __attribute__((aligned(16))) float w_lds[EPAD * (kRouteChunk + kRoutePad)];  // [e][j]
+  constexpr int kGroups = 64 / L;  // token groups per wave
   constexpr int kTokPerWave = kGroups * R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = lane % EP, grp = lane / EP;
+  const int le = lane % L, grp = lane / L;
   const int64_t tok0 = (static_cast<int64_t>(blockIdx.x) * (kRouteThreads / 64) + wave) * kTokPerWave;
 
   // Token rows this lane evaluates (clamped for the tail; not stored).
@@ -63,94 +69,133 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const T* __restric
     if (t >= ntok) t = ntok - 1;
     xrow[r] = x + t * d;
   }
-  float acc[R];
+  float acc[P][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int q = 0; q < P; ++q)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[q][r] = 0.0f;
 
   constexpr int kStride = kRouteChunk + kRoutePad;
   for (int j0 = 0; j0 < d; j0 += kRouteChunk) {
     const int jn = min(kRouteChunk, d - j0);
     __syncthreads();
     // Stage W[j0 .. j0+jn)[0 .. E) transposed to [e][j].
-    for (int i = threadIdx.x; i < jn * EP; i += kRouteThreads) {
-      const int jj = i / EP, ee = i % EP;
+    for (int i = threadIdx.x; i < jn * EPAD; i += kRouteThreads) {
+      const int jj = i / EPAD, ee = i % EPAD;
       w_lds[ee * kStride + jj] = (ee < E) ? wr[static_cast<int64_t>(j0 + jj) * E + ee] : 0.0f;
     }
     __syncthreads();
-    const float* wl = w_lds + e * kStride;
     for (int jj = 0; jj < jn; jj += 8) {
-      float4 w0 = *reinterpret_cast<const float4*>(wl + jj);
-      float4 w1 = *reinterpret_cast<const float4*>(wl + jj + 4);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float wv[P][8];
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const float* wl = w_lds + (le + q * L) * kStride + jj;
+        const float4 w0 = *reinterpret_cast<const float4*>(wl);
+        const float4 w1 = *reinterpret_cast<const float4*>(wl + 4);
+        wv[q][0] = w0.x; wv[q][1] = w0.y; wv[q][2] = w0.z; wv[q][3] = w0.w;
+        wv[q][4] = w1.x; wv[q][5] = w1.y; wv[q][6] = w1.z; wv[q][7] = w1.w;
+      }
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float xv[8];
         load8(xrow[r] + j0 + jj, xv);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[r] = __builtin_fmaf(xv[q], wv[q], acc[r]);
+        for (int jq = 0; jq < 8; ++jq)
+#pragma unroll
+          for (int q = 0; q < P; ++q) acc[q][r] = __builtin_fmaf(xv[jq], wv[q][jq], acc[q][r]);
       }
     }
   }
 
-  // Top-k per token: k rounds of a butterfly argmax within the EP-lane group.
+  // Top-k per token: k rounds of argmax, first over the lane's own P
+  // experts, then a butterfly over the L lanes of the group.
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t t = tok0 + grp * R + r;
-    const float v = acc[r];
-    bool taken = (e >= E);
-    float my_v = 0.0f, vmax = 0.0f;
-    int my_e = 0;
-    for (int i = 0; i < k; ++i) {
-      float bv = v;
-      int be = taken ? (0x10000 + e) : e;
+    bool taken[P];
 #pragma unroll
-      for (int off = EP / 2; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, EP);
-        const int oe = __shfl_xor(be, off, EP);
+    for (int q = 0; q < P; ++q) taken[q] = (le + q * L) >= E;
+    // Rank i (< k <= L * P) is kept by lane i % L of the group, in slot i / L.
+    float my_v[P], vmax = 0.0f;
+    int my_e[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      my_v[q] = 0.0f;
+      my_e[q] = 0;
+    }
+    for (int i = 0; i < k; ++i) {
+      float bv = acc[0][r];
+      int be = taken[0] ? (0x10000 + le) : le;
+#pragma unroll
+      for (int q = 1; q < P; ++q) {
+        const int eq = le + q * L;
+        const int ce = taken[q] ? (0x10000 + eq) : eq;
+        if (ranks_before(acc[q][r], ce, bv, be)) {
+          bv = acc[q][r];
+          be = ce;
+        }
+      }
+#pragma unroll
+      for (int off = L / 2; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, L);
+        const int oe = __shfl_xor(be, off, L);
         if (ranks_before(ov, oe, bv, be)) {
           bv = ov;
           be = oe;
         }
       }
       if (i == 0) vmax = bv;
-      if (be == e) taken = true;
-      if (e == i) {
-        my_v = bv;
-        my_e = be;
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        if (be == le + q * L) taken[q] = true;
+        if (i == q * L + le) {
+          my_v[q] = bv;
+          my_e[q] = be;
+        }
       }
     }
-    float u = (e < k) ? expf(my_v - vmax) : 0.0f;
-    float sum = u;
+    // Weights exp(l_i - l_0) / sum over the k kept ranks.
+    float u[P], sum = 0.0f;
 #pragma unroll
-    for (int off = EP / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, EP);
-    if (e < k && t < ntok) {
-      topk_idx[t * k + e] = my_e;
-      topk_w[t * k + e] = u / sum;
+    for (int q = 0; q < P; ++q) {
+      u[q] = (q * L + le < k) ? expf(my_v[q] - vmax) : 0.0f;
+      sum += u[q];
+    }
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, L);
+    if (t < ntok) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int i = q * L + le;
+        if (i < k) {
+          topk_idx[t * k + i] = my_e[q];
+          topk_w[t * k + i] = u[q] / sum;
+        }
+      }
     }
   }
 }
 
-template <typename T, int EP, int R>
+template <typename T, int L, int P, int R>
 hipError_t launch_route_t(const void* x, const float* wr, int64_t T_, int d, int E, int k,
                           int32_t* idx, float* w, hipStream_t s) {
-  constexpr int kTokPerBlock = (kRouteThreads / 64) * (64 / EP) * R;
+  constexpr int kTokPerBlock = (kRouteThreads / 64) * (64 / L) * R;
   const int64_t blocks = (T_ + kTokPerBlock - 1) / kTokPerBlock;
-  MOE_LAUNCH("route", (route_kernel<T, EP, R>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kRouteThreads), 0, s, static_cast<const T*>(x), wr, T_, d, E, k, idx,
-                     w);
+  MOE_LAUNCH("route", (route_kernel<T, L, P, R>), dim3(static_cast<unsigned>(blocks)),
+             dim3(kRouteThreads), 0, s, static_cast<const T*>(x), wr, T_, d, E, k, idx, w);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_route_dt(const void* x, const float* wr, int64_t T_, int d, int E, int k,
                            int32_t* idx, float* w, hipStream_t s) {
-  if (E <= 1) return launch_route_t<T, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 2) return launch_route_t<T, 2, 1>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 4) return launch_route_t<T, 4, 1>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 8) return launch_route_t<T, 8, 2>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 16) return launch_route_t<T, 16, 4>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 32) return launch_route_t<T, 32, 8>(x, wr, T_, d, E, k, idx, w, s);
-  return launch_route_t<T, 64, 8>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 1) return launch_route_t<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 2) return launch_route_t<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 4) return launch_route_t<T, 4, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 8) return launch_route_t<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 16) return launch_route_t<T, 4, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 32) return launch_route_t<T, 8, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
+  return launch_route_t<T, 16, 4, 8>(x, wr, T_, d, E, k, idx, w, s);
 }
 
 }  // namespace
