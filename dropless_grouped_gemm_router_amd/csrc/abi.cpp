@@ -146,12 +146,19 @@ MOE_EXPORT int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w
                        size_t workspace_bytes, void* stream) {
   int st = check(p);
   if (st != MOE_OK) return st;
-  if (!g || !ok_ptr(g->w_router, 4)) return MOE_ERR_INVALID;
+  // The backward GEMMs tile the hidden widths by 128.
+  if (p->d_hidden % 128 != 0 || p->d_shared % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!g || !ok_ptr(g->w_router, 4) || !ok_ptr(g->w_gate) || !ok_ptr(g->w_up) ||
+      !ok_ptr(g->w_down))
+    return MOE_ERR_INVALID;
+  if (p->d_shared > 0 && (!ok_ptr(g->ws_gate) || !ok_ptr(g->ws_up) || !ok_ptr(g->ws_down)))
+    return MOE_ERR_INVALID;
   if (p->tokens == 0) {
     // Nothing flows back from zero tokens, yet the gradients are defined
     // (zero) and fully overwritten.
-    return hip_status(moe::launch_bwd(*p, x, *w, *r, y_sorted, saved, grad_out, grad_x, *g,
-                                      workspace, as_stream(stream)));
+    return hip_status(moe::launch_bwd(*p, x, w ? *w : moe_weights{}, r ? *r : moe_routing{},
+                                      y_sorted, saved, grad_out, grad_x, *g, workspace,
+                                      as_stream(stream)));
   }
   if (!w || !r || !ok_ptr(x) || !ok_ptr(w->w_router, 4) || !ok_ptr(w->w_gate) || !ok_ptr(w->w_up) ||
       !ok_ptr(w->w_down) || !ok_ptr(r->topk_idx, 4) || !ok_ptr(r->topk_w, 4) ||

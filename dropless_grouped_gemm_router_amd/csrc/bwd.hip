@@ -1,15 +1,472 @@
-// Train-step backward (gpu_moe_h100.json header: value and gradient with
-// respect to the parameters and the input).
+// Train-step backward of the dropless MoE layer (gpu_moe_h100.json header:
+// value and gradient with respect to the parameters and the input) for
+// L = sum(out * G), with the top-k selection held fixed.
+//
+//   combine:  dY[slot(t,i)] = w_i G_t,  dw_i = <G_t, y[slot(t,i)]>
+//   router:   dl_i = w_i (dw_i - sum_j w_j dw_j);  dW_r = x^T dl;  dx += dl W_r^T
+//   experts:  dH = dY W_down^T -> (dA, dB) through SwiGLU with the saved
+//             pre-activations; dX_sorted = dA W_gate^T + dB W_up^T;
+//             dW_down = H^T dY, dW_gate = X^T dA, dW_up = X^T dB per expert
+//   shared:   the same chain with weight 1 over all tokens
+//   dx[t] = sum_i dX_sorted[slot(t,i)] + router term + shared term
+//
+// Every reduction runs in a fixed order with one writer per output (no
+// floating-point atomics), so the gradients are deterministic.
 #include "gemm_core.h"
 
 namespace moe {
 
-size_t bwd_ws_bytes(const moe_problem&) { return 0; }
+namespace {
 
-hipError_t launch_bwd(const moe_problem&, const void*, const moe_weights&, const moe_routing&,
-                      const void*, const void*, const void*, void*, const moe_grads&, void*,
-                      hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kRowThreads = 256;
+
+template <typename T>
+struct V16;  // one 16-byte piece of a row
+template <>
+struct V16<bf16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const bf16_t* p, float* o) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    o[0] = bf16lo(v.x); o[1] = bf16hi(v.x); o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
+    o[4] = bf16lo(v.z); o[5] = bf16hi(v.z); o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
+  }
+  __device__ static void store(bf16_t* p, const float* o) {
+    uint4 v;
+    v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
+    v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+};
+template <>
+struct V16<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+  __device__ static void store(float* p, const float* o) {
+    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// One wave per token: dY rows, dw by wave reduction, then dl for the kept
+// experts (lane i holds rank i; k <= 64).
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
+    int64_t ntok, int k, int d, const T* __restrict__ G, const T* __restrict__ y,
+    const float* __restrict__ w, const int32_t* __restrict__ inv_perm, T* __restrict__ dY,
+    float* __restrict__ dl) {
+  constexpr int N = V16<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  float my_dw = 0.0f, my_w = 0.0f;
+  for (int i = 0; i < k; ++i) {
+    const int64_t slot = inv_perm[t * k + i];
+    const float wi = w[t * k + i];
+    float dot = 0.0f;
+    for (int c = lane * N; c < d; c += 64 * N) {
+      float g[N], yv[N], o[N];
+      V16<T>::load(G + t * d + c, g);
+      V16<T>::load(y + slot * d + c, yv);
+#pragma unroll
+      for (int q = 0; q < N; ++q) {
+        dot = __builtin_fmaf(g[q], yv[q], dot);
+        o[q] = wi * g[q];
+      }
+      V16<T>::store(dY + slot * d + c, o);
+    }
+    dot = wave_sum(dot);
+    if (lane == i) {
+      my_dw = dot;
+      my_w = wi;
+    }
+  }
+  const float s = wave_sum(lane < k ? my_w * my_dw : 0.0f);
+  if (lane < k) dl[t * k + lane] = my_w * (my_dw - s);
+}
+
+// Router weight gradient, stage 1: per tile of sorted rows (one expert),
+// partial[tile][j] = sum over the tile's rows, in order, of x[tok][j] * dl[slot].
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void router_partial_kernel(
+    const T* __restrict__ x, int d, int topk, const int32_t* __restrict__ perm,
+    const float* __restrict__ dl, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, float* __restrict__ partial) {
+  __shared__ int64_t tok[128];
+  __shared__ float dv[128];
+  const int tile = blockIdx.x;
+  if (tile >= *num_tiles) return;
+  const int row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
+  for (int r = threadIdx.x; r < rows; r += kRowThreads) {
+    const int32_t s = perm[row0 + r];
+    tok[r] = s / topk;
+    dv[r] = dl[s];
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += kRowThreads) {
+    float acc = 0.0f;
+    for (int r = 0; r < rows; ++r) {
+      float xv;
+      if constexpr (sizeof(T) == 2) xv = bf16_to_f32(x[tok[r] * d + j]);
+      else xv = x[tok[r] * d + j];
+      acc = __builtin_fmaf(xv, dv[r], acc);
+    }
+    partial[static_cast<int64_t>(tile) * d + j] = acc;
+  }
+}
+
+// Stage 2: dW_r[j][e] = sum of expert e's tile partials, in tile order.
+__global__ __launch_bounds__(kRowThreads) void router_reduce_kernel(
+    const float* __restrict__ partial, const int32_t* __restrict__ offsets, int E, int bm, int d,
+    float* __restrict__ dwr) {
+  __shared__ int32_t first, cnt;
+  const int e = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int32_t n = 0;
+    for (int q = 0; q < e; ++q) n += (offsets[q + 1] - offsets[q] + bm - 1) / bm;
+    first = n;
+    cnt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < d; j += kRowThreads) {
+    float acc = 0.0f;
+    for (int n = 0; n < cnt; ++n) acc += partial[static_cast<int64_t>(first + n) * d + j];
+    dwr[static_cast<int64_t>(j) * E + e] = acc;
+  }
+}
+
+// dx[t] = sum_i dX_sorted[slot(t,i)] + sum_i dl_i W_r[:, e_i] + dx_shared[t].
+template <typename T>
+__global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
+    int64_t ntok, int k, int d, int E, const T* __restrict__ dxs, const int32_t* __restrict__ inv_perm,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
+    const float* __restrict__ wr, const T* __restrict__ dx_shared, T* __restrict__ dx) {
+  constexpr int N = V16<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  for (int c = lane * N; c < d; c += 64 * N) {
+    float acc[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+    for (int i = 0; i < k; ++i) {
+      const int64_t slot = inv_perm[t * k + i];
+      const int e = topk_idx[t * k + i];
+      const float li = dl[t * k + i];
+      float v[N];
+      V16<T>::load(dxs + slot * d + c, v);
+#pragma unroll
+      for (int q = 0; q < N; ++q)
+        acc[q] += __builtin_fmaf(li, wr[static_cast<int64_t>(c + q) * E + e], v[q]);
+    }
+    if (dx_shared) {
+      float v[N];
+      V16<T>::load(dx_shared + t * d + c, v);
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += v[q];
+    }
+    V16<T>::store(dx + t * d + c, acc);
+  }
+}
+
+// Fixed-order sum of split-K partials [splits][M][N]; columns n >= nsplit
+// go to c2 at column n - nsplit.
+__global__ __launch_bounds__(kRowThreads) void split_reduce_kernel(
+    const float* __restrict__ partial, int splits, int64_t M, int N, int nsplit, int64_t ldc,
+    float* __restrict__ c, float* __restrict__ c2) {
+  const int64_t MN = M * N;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x; i < MN;
+       i += static_cast<int64_t>(gridDim.x) * kRowThreads) {
+    float acc = 0.0f;
+    for (int s = 0; s < splits; ++s) acc += partial[s * MN + i];
+    const int64_t m = i / N;
+    const int n = static_cast<int>(i % N);
+    if (n < nsplit) c[m * ldc + n] = acc;
+    else c2[m * ldc + (n - nsplit)] = acc;
+  }
+}
+
+__global__ __launch_bounds__(kRowThreads) void fill_zero_kernel(float* __restrict__ p, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kRowThreads)
+    p[i] = 0.0f;
+}
+
+struct BwdLayout {
+  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, total;
+  int ks_sd, ks_sgu;
+};
+
+int split_count(int64_t rows, int tiles) {
+  int ks = (512 + tiles - 1) / tiles;
+  ks = ks < 1 ? 1 : (ks > 64 ? 64 : ks);
+  if (ks > rows) ks = static_cast<int>(rows > 0 ? rows : 1);
+  return ks;
+}
+
+BwdLayout bwd_layout(const moe_problem& p) {
+  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
+  const size_t T = static_cast<size_t>(p.tokens), S = T * p.top_k;
+  const size_t d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+  const size_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
+  BwdLayout L{};
+  L.ks_sd = hs ? split_count(p.tokens, static_cast<int>((hs / 128) * (d / 128))) : 0;
+  L.ks_sgu = hs ? split_count(p.tokens, static_cast<int>((d / 128) * (2 * hs / 128))) : 0;
+  size_t o = 0;
+  L.dY = o;       o = align_up(o + S * d * es, 256);
+  L.dl = o;       o = align_up(o + S * 4, 256);
+  L.dAB = o;      o = align_up(o + S * 2 * h * es, 256);
+  L.dXs = o;      o = align_up(o + S * d * es, 256);
+  L.rpart = o;    o = align_up(o + max_tiles * d * 4, 256);
+  L.dABs = o;     o = align_up(o + T * 2 * hs * es, 256);
+  L.dxs = o;      o = align_up(o + T * d * es, 256);
+  L.part_sd = o;  o = align_up(o + static_cast<size_t>(L.ks_sd) * hs * d * 4, 256);
+  L.part_sgu = o; o = align_up(o + static_cast<size_t>(L.ks_sgu) * d * 2 * hs * 4, 256);
+  L.total = o;
+  return L;
+}
+
+void zero(float* p, int64_t n, hipStream_t s) {
+  if (!p || n <= 0) return;
+  int64_t blocks = (n + kRowThreads - 1) / kRowThreads;
+  if (blocks > 4096) blocks = 4096;
+  MOE_LAUNCH("fill_zero", fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRowThreads),
+             0, s, p, n);
+}
+
+template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
+void gemm(const char* name, const GemmArgs& a, int64_t row_tiles, hipStream_t s) {
+  if (row_tiles <= 0) return;
+  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), gemm_grid<Cfg>(row_tiles, a.N),
+             dim3(256), 0, s, a);
+}
+
+template <typename T, bool kGatherA, bool kDense>
+void wgrad(const char* name, const WgradArgs& a, int groups, hipStream_t s) {
+  const int64_t blocks = static_cast<int64_t>(groups) * (a.M / 128) * (a.N / 128);
+  if (blocks <= 0) return;
+  MOE_LAUNCH(name, (wgrad_kernel<T, kGatherA, kDense>), dim3(static_cast<unsigned>(blocks)),
+             dim3(256), 0, s, a);
+}
+
+template <typename T, typename Cfg>
+void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
+                  const void* saved_ab, const void* dY, void* dAB, void* dXs, hipStream_t s) {
+  const int64_t S = p.tokens * p.top_k;
+  const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
+  const int d = p.d_model, h = p.d_hidden;
+  GemmArgs a{};
+  a.a = dY;
+  a.lda = d;
+  a.b = w.w_down;  // [E][h][d]: row n = hidden unit, K = d contiguous
+  a.b_group_stride = static_cast<int64_t>(h) * d;
+  a.N = h;
+  a.K = d;
+  a.tiles = r.tiles;
+  a.num_tiles = r.num_tiles;
+  a.c = dAB;
+  a.ldc = 2 * static_cast<int64_t>(h);
+  a.hsplit = h;
+  a.sa = const_cast<void*>(saved_ab);
+  a.sb = const_cast<T*>(static_cast<const T*>(saved_ab) + h);
+  a.lds = 2 * static_cast<int64_t>(h);
+  gemm<T, Cfg, false, kEpiSwigluBwd, false>("bwd_down_dgrad", a, max_tiles, s);
+
+  GemmArgs b{};
+  b.a = dAB;
+  b.lda = 2 * static_cast<int64_t>(h);
+  b.b = w.w_gate;  // [E][d][h]: row n = model unit, K = h contiguous
+  b.b_group_stride = static_cast<int64_t>(d) * h;
+  b.ldb = h;
+  b.b2 = w.w_up;
+  b.b2_group_stride = static_cast<int64_t>(d) * h;
+  b.ksplit = h;
+  b.N = d;
+  b.K = 2 * h;
+  b.tiles = r.tiles;
+  b.num_tiles = r.num_tiles;
+  b.c = dXs;
+  b.ldc = d;
+  gemm<T, Cfg, false, kEpiStore, false>("bwd_gate_up_dgrad", b, max_tiles, s);
+}
+
+template <typename T>
+hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, const moe_routing& r,
+                 const void* y_sorted, const void* saved, const void* grad_out, void* grad_x,
+                 const moe_grads& g, void* ws, hipStream_t s) {
+  const int64_t T_ = p.tokens, S = T_ * p.top_k;
+  const int E = p.experts, k = p.top_k, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+  const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + E;
+  const BwdLayout L = bwd_layout(p);
+  const FfnLayout F = ffn_layout(p, true);
+  char* W = static_cast<char*>(ws);
+  const char* SV = static_cast<const char*>(saved);
+  T* dY = reinterpret_cast<T*>(W + L.dY);
+  float* dl = reinterpret_cast<float*>(W + L.dl);
+  T* dAB = reinterpret_cast<T*>(W + L.dAB);
+  T* dXs = reinterpret_cast<T*>(W + L.dXs);
+  float* rpart = reinterpret_cast<float*>(W + L.rpart);
+  const int64_t row_blocks = (T_ + kRowThreads / 64 - 1) / (kRowThreads / 64);
+
+  // a11: combine backward and per-slot router gradient
+  MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
+             dim3(kRowThreads), 0, s, T_, k, d, static_cast<const T*>(grad_out),
+             static_cast<const T*>(y_sorted), r.topk_w, r.inv_perm, dY, dl);
+  // a12: router weight gradient (tile partials, then a per-expert ordered sum)
+  MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
+             dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl, r.tiles,
+             r.num_tiles, rpart);
+  MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
+             r.expert_offsets, E, p.block_m, d, g.w_router);
+  // a13 + a15: dgrad GEMMs
+  const void* sab = SV + F.sv_ab;
+  switch (p.block_m) {
+    case 32: routed_dgrad<T, Cfg32>(p, w, r, sab, dY, dAB, dXs, s); break;
+    case 64: routed_dgrad<T, Cfg64>(p, w, r, sab, dY, dAB, dXs, s); break;
+    default: routed_dgrad<T, Cfg128>(p, w, r, sab, dY, dAB, dXs, s); break;
+  }
+  // a14: per-expert weight gradients, K = the expert's rows
+  {
+    WgradArgs a{};
+    a.a = SV + F.sv_h;
+    a.lda = h;
+    a.b = dY;
+    a.ldb = d;
+    a.M = h;
+    a.N = d;
+    a.row_offsets = r.expert_offsets;
+    a.c = g.w_down;
+    a.nsplit = d;
+    a.ldc = d;
+    a.c_group_stride = static_cast<int64_t>(h) * d;
+    wgrad<T, false, false>("bwd_wgrad_down", a, E, s);
+    WgradArgs b{};
+    b.a = x;
+    b.lda = d;
+    b.perm = r.perm;
+    b.topk = k;
+    b.b = dAB;
+    b.ldb = 2 * static_cast<int64_t>(h);
+    b.M = d;
+    b.N = 2 * h;
+    b.row_offsets = r.expert_offsets;
+    b.c = g.w_gate;
+    b.c2 = g.w_up;
+    b.nsplit = h;
+    b.ldc = h;
+    b.c_group_stride = static_cast<int64_t>(d) * h;
+    wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, s);
+  }
+  // a16: shared expert
+  T* dxs = nullptr;
+  if (hs > 0) {
+    T* dABs = reinterpret_cast<T*>(W + L.dABs);
+    dxs = reinterpret_cast<T*>(W + L.dxs);
+    const int64_t row_tiles = (T_ + Cfg128::BM - 1) / Cfg128::BM;
+    const T* ssab = reinterpret_cast<const T*>(SV + F.sv_sab);
+    GemmArgs a{};
+    a.a = grad_out;
+    a.lda = d;
+    a.b = w.ws_down;  // [hs][d]
+    a.N = hs;
+    a.K = d;
+    a.M = T_;
+    a.c = dABs;
+    a.ldc = 2 * static_cast<int64_t>(hs);
+    a.hsplit = hs;
+    a.sa = const_cast<T*>(ssab);
+    a.sb = const_cast<T*>(ssab + hs);
+    a.lds = 2 * static_cast<int64_t>(hs);
+    gemm<T, Cfg128, false, kEpiSwigluBwd, true>("bwd_shared_down_dgrad", a, row_tiles, s);
+    GemmArgs b{};
+    b.a = dABs;
+    b.lda = 2 * static_cast<int64_t>(hs);
+    b.b = w.ws_gate;  // [d][hs]
+    b.ldb = hs;
+    b.b2 = w.ws_up;
+    b.ksplit = hs;
+    b.N = d;
+    b.K = 2 * hs;
+    b.M = T_;
+    b.c = dxs;
+    b.ldc = d;
+    gemm<T, Cfg128, false, kEpiStore, true>("bwd_shared_gate_up_dgrad", b, row_tiles, s);
+
+    float* p1 = reinterpret_cast<float*>(W + L.part_sd);
+    WgradArgs c{};
+    c.a = SV + F.sv_sh;
+    c.lda = hs;
+    c.b = grad_out;
+    c.ldb = d;
+    c.M = hs;
+    c.N = d;
+    c.rows_total = T_;
+    c.splits = L.ks_sd;
+    c.c = p1;
+    c.nsplit = d;
+    c.ldc = d;
+    c.c_group_stride = static_cast<int64_t>(hs) * d;
+    wgrad<T, false, true>("bwd_shared_wgrad_down", c, L.ks_sd, s);
+    MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p1,
+               L.ks_sd, static_cast<int64_t>(hs), d, d, static_cast<int64_t>(d), g.ws_down,
+               static_cast<float*>(nullptr));
+    float* p2 = reinterpret_cast<float*>(W + L.part_sgu);
+    WgradArgs e{};
+    e.a = x;
+    e.lda = d;
+    e.b = dABs;
+    e.ldb = 2 * static_cast<int64_t>(hs);
+    e.M = d;
+    e.N = 2 * hs;
+    e.rows_total = T_;
+    e.splits = L.ks_sgu;
+    e.c = p2;
+    e.nsplit = 2 * hs;
+    e.ldc = 2 * static_cast<int64_t>(hs);
+    e.c_group_stride = static_cast<int64_t>(d) * 2 * hs;
+    wgrad<T, false, true>("bwd_shared_wgrad_gate_up", e, L.ks_sgu, s);
+    MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p2,
+               L.ks_sgu, static_cast<int64_t>(d), 2 * hs, hs, static_cast<int64_t>(hs), g.ws_gate,
+               g.ws_up);
+  }
+  // dx: gather-sum of the routed input gradients plus the router and shared terms
+  MOE_LAUNCH("bwd_dx", dx_gather_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
+             dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, w.w_router,
+             static_cast<const T*>(dxs), static_cast<T*>(grad_x));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_ws_bytes(const moe_problem& p) { return bwd_layout(p).total; }
+
+hipError_t launch_bwd(const moe_problem& p, const void* x, const moe_weights& w,
+                      const moe_routing& r, const void* y_sorted, const void* saved,
+                      const void* grad_out, void* grad_x, const moe_grads& g, void* ws,
+                      hipStream_t s) {
+  if (p.tokens == 0) {
+    const int64_t E = p.experts, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+    zero(g.w_router, d * E, s);
+    zero(g.w_gate, E * d * h, s);
+    zero(g.w_up, E * d * h, s);
+    zero(g.w_down, E * h * d, s);
+    if (hs > 0) {
+      zero(g.ws_gate, d * hs, s);
+      zero(g.ws_up, d * hs, s);
+      zero(g.ws_down, hs * d, s);
+    }
+    return hipGetLastError();
+  }
+  if (p.dtype == MOE_BF16)
+    return bwd_t<bf16_t>(p, x, w, r, y_sorted, saved, grad_out, grad_x, g, ws, s);
+  return bwd_t<float>(p, x, w, r, y_sorted, saved, grad_out, grad_x, g, ws, s);
 }
 
 }  // namespace moe

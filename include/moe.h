@@ -229,6 +229,10 @@ int moe_combine(const moe_problem* p, const void* y_sorted, const moe_routing* r
  * forward, and grad_out [tokens, d_model] (dtype). Writes grad_x
  * [tokens, d_model] (dtype) and every array of g (fp32; the shared ones
  * only when d_shared > 0). workspace: >= moe_workspace_bytes(p, 1).
+ * saved must be the moe_saved_bytes(p) buffer moe_ffn_fwd filled.
+ * Needs d_hidden and d_shared to be multiples of 128 (else
+ * MOE_ERR_UNSUPPORTED). With tokens == 0 the weight gradients are zeroed
+ * and nothing else is touched.
  */
 int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w, const moe_routing* r,
             const void* y_sorted, const void* saved, const void* grad_out, void* grad_x,

@@ -89,7 +89,7 @@ def fake_weights(base=0x20000000, shared=True):
     return {n: FakeTensor(base + i * 0x100000) for i, n in enumerate(names)}
 
 
-P = Problem(100, 8, 2, 256, 128, 64, "bf16", 64)
+P = Problem(100, 8, 2, 256, 128, 128, "bf16", 64)
 
 
 def expect(code, fn, *a, **k):
@@ -153,9 +153,13 @@ def test_bwd_argument_errors():
            ws, workspace_bytes=need, stream=0)
     expect(B.MOE_ERR_INVALID, B.moe_bwd, P, x, w, r, a[0], None, a[2], a[3], g, ws,
            workspace_bytes=need, stream=0)
-    if need > B.moe_workspace_bytes(P, training=False):
-        expect(B.MOE_ERR_WORKSPACE, B.moe_bwd, P, x, w, r, a[0], a[1], a[2], a[3], g, ws,
-               workspace_bytes=need - 1, stream=0)
+    assert need > B.moe_workspace_bytes(P, training=False)
+    expect(B.MOE_ERR_WORKSPACE, B.moe_bwd, P, x, w, r, a[0], a[1], a[2], a[3], g, ws,
+           workspace_bytes=need - 1, stream=0)
+    # the backward tiles hidden widths by 128
+    p64 = Problem(100, 8, 2, 256, 192, 128, "bf16", 64)
+    expect(B.MOE_ERR_UNSUPPORTED, B.moe_bwd, p64, x, w, r, a[0], a[1], a[2], a[3], g, ws,
+           workspace_bytes=need, stream=0)
 
 
 def test_buffer_layouts_match_pages_argument_bytes():

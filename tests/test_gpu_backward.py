@@ -1,0 +1,102 @@
+"""HIP train-step backward vs the oracle, through the C ABI (GPU)."""
+
+import numpy as np
+import pytest
+
+from dropless_grouped_gemm_router_amd import binding as B
+from dropless_grouped_gemm_router_amd.inputs import Problem, WORKLOADS
+from oracle import oracle
+
+from gpu_util import TOL, Case, note, to_np
+
+pytestmark = pytest.mark.gpu
+
+GRAD_NAMES = ["w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"]
+
+
+def run_bwd(c: Case):
+    import torch
+    c.forward()
+    gx, g = B.backward(c.p, c.dev["x"], c.weights(), c.dev["grad_out"], c.buf)
+    torch.cuda.synchronize()
+    return gx, g
+
+
+def check_grads(c: Case, gx, g, nthreads=0):
+    p, v = c.p, c.v
+    idx = c.buf.routing["topk_idx"].cpu().numpy()
+    _, idx_ref, w = oracle.route(v["x"], v["w_router"], p.top_k, nthreads)
+    assert np.array_equal(idx, idx_ref)
+    ref = oracle.backward(v["x"], v["w_router"], v["w_gate"], v["w_up"], v["w_down"],
+                          v["grad_out"], idx_ref, w, *c.shared(), nthreads=nthreads)
+    errs = {"x": oracle.rel_err(to_np(gx), ref["x"])}
+    for n in GRAD_NAMES:
+        if n in g:
+            errs[n] = oracle.rel_err(to_np(g[n]), ref[n])
+    note(f"grad rel errs: " + ", ".join(f"{k} {e:.2e}" for k, e in errs.items()))
+    for n, e in errs.items():
+        assert e < TOL[p.dtype], (n, e)
+    return ref
+
+
+SMALL = [
+    Problem(300, 8, 2, 256, 128, 0, "bf16", 64),
+    Problem(300, 8, 2, 256, 128, 0, "fp32", 64),
+    Problem(517, 16, 4, 256, 256, 128, "bf16", 128),
+    Problem(517, 16, 4, 256, 128, 128, "fp32", 32),
+    Problem(3, 4, 2, 128, 128, 128, "bf16", 32),
+    Problem(200, 5, 5, 128, 128, 0, "fp32", 64),
+    Problem(1000, 64, 8, 128, 128, 256, "bf16", 128),
+]
+
+
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}")
+def test_backward_small_elementwise(p):
+    note(f"backward small {p}")
+    c = Case(p, seed=11, training=True)
+    gx, g = run_bwd(c)
+    check_grads(c, gx, g)
+
+
+def test_top1_router_gradient_exactly_zero():
+    p = Problem(150, 8, 1, 128, 128, 0, "bf16", 64)
+    c = Case(p, seed=2, training=True)
+    gx, g = run_bwd(c)
+    assert bool((g["w_router"] == 0).all())
+    check_grads(c, gx, g)
+
+
+def test_backward_deterministic():
+    p = Problem(700, 16, 4, 256, 128, 128, "bf16", 64)
+    c = Case(p, seed=4, training=True)
+    gx, g = run_bwd(c)
+    a = {n: t.clone() for n, t in g.items()}
+    ax = gx.clone()
+    gx2, g2 = run_bwd(c)
+    assert bool((ax == gx2).all())
+    for n in a:
+        assert bool((a[n] == g2[n]).all()), n
+
+
+def test_zero_tokens_zeroes_weight_grads():
+    import torch
+    p = Problem(0, 8, 2, 256, 128, 128, "bf16", 64)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    g = dict(w_router=torch.ones((256, 8), **f32), w_gate=torch.ones((8, 256, 128), **f32),
+             w_up=torch.ones((8, 256, 128), **f32), w_down=torch.ones((8, 128, 256), **f32),
+             ws_gate=torch.ones((256, 128), **f32), ws_up=torch.ones((256, 128), **f32),
+             ws_down=torch.ones((128, 256), **f32))
+    B.moe_bwd(p, None, {}, {}, None, None, None, None, g, None, workspace_bytes=0)
+    torch.cuda.synchronize()
+    for n, t in g.items():
+        assert bool((t == 0).all()), n
+
+
+def test_train_workload_full_size():
+    """The train-step workload (16384 tokens, E64 top-8, d512 h128, shared
+    1024) at full size: every gradient element against the oracle."""
+    name, p, _ = WORKLOADS[4]
+    note(f"workload 4: {name}")
+    c = Case(p, seed=0, training=True)
+    gx, g = run_bwd(c)
+    check_grads(c, gx, g)
