@@ -70,7 +70,20 @@ def main():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--cpu-sample", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (counter calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               "requested); see the sharding paragraph of the design notes.", file=sys.stderr)

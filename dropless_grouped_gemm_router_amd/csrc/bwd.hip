@@ -243,10 +243,39 @@ void zero(float* p, int64_t n, hipStream_t s) {
 
 template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
 void gemm(const char* name, const GemmArgs& a, int64_t row_tiles, hipStream_t s) {
+  if (kDense) row_tiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   if (row_tiles <= 0) return;
-  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), gemm_grid<Cfg>(row_tiles, a.N),
-             dim3(256), 0, s, a);
+  const int64_t work = row_tiles * (a.N / Cfg::BN);
+  const int slots = persistent_slots(
+      reinterpret_cast<const void*>(&gemm_kernel<T, Cfg, kGather, kEpi, kDense>), Cfg::NT);
+  const unsigned grid = static_cast<unsigned>(work < slots ? work : slots);
+  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), dim3(grid), dim3(Cfg::NT), 0, s,
+             a, static_cast<int>(work));
 }
+
+// Grouped GEMM over the block_m tile list: the eight-wave 256-column tile
+// when N allows it, else the four-wave 128-column tile.
+template <typename T, bool kGather, int kEpi>
+void grouped_gemm(const char* name, const GemmArgs& a, int bm, int64_t max_tiles, hipStream_t s) {
+  const bool wide = a.N % 256 == 0;
+  if (bm == 128) {
+    if (wide) gemm<T, Cfg128W, kGather, kEpi, false>(name, a, max_tiles, s);
+    else gemm<T, Cfg128, kGather, kEpi, false>(name, a, max_tiles, s);
+  } else if (bm == 64) {
+    if (wide) gemm<T, Cfg64W, kGather, kEpi, false>(name, a, max_tiles, s);
+    else gemm<T, Cfg64, kGather, kEpi, false>(name, a, max_tiles, s);
+  } else {
+    gemm<T, Cfg32, kGather, kEpi, false>(name, a, max_tiles, s);
+  }
+}
+
+// Dense GEMM over all rows (shared expert).
+template <typename T, int kEpi>
+void dense_gemm(const char* name, const GemmArgs& a, hipStream_t s) {
+  if (a.N % 256 == 0) gemm<T, Cfg128W, false, kEpi, true>(name, a, 1, s);
+  else gemm<T, Cfg128, false, kEpi, true>(name, a, 1, s);
+}
+
 
 template <typename T, bool kGatherA, bool kDense>
 void wgrad(const char* name, const WgradArgs& a, int groups, hipStream_t s) {
@@ -256,7 +285,7 @@ void wgrad(const char* name, const WgradArgs& a, int groups, hipStream_t s) {
              dim3(256), 0, s, a);
 }
 
-template <typename T, typename Cfg>
+template <typename T>
 void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
                   const void* saved_ab, const void* dY, void* dAB, void* dXs, hipStream_t s) {
   const int64_t S = p.tokens * p.top_k;
@@ -277,7 +306,7 @@ void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing&
   a.sa = const_cast<void*>(saved_ab);
   a.sb = const_cast<T*>(static_cast<const T*>(saved_ab) + h);
   a.lds = 2 * static_cast<int64_t>(h);
-  gemm<T, Cfg, false, kEpiSwigluBwd, false>("bwd_down_dgrad", a, max_tiles, s);
+  grouped_gemm<T, false, kEpiSwigluBwd>("bwd_down_dgrad", a, p.block_m, max_tiles, s);
 
   GemmArgs b{};
   b.a = dAB;
@@ -294,7 +323,7 @@ void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing&
   b.num_tiles = r.num_tiles;
   b.c = dXs;
   b.ldc = d;
-  gemm<T, Cfg, false, kEpiStore, false>("bwd_gate_up_dgrad", b, max_tiles, s);
+  grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, p.block_m, max_tiles, s);
 }
 
 template <typename T>
@@ -327,11 +356,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
              r.expert_offsets, E, p.block_m, d, g.w_router);
   // a13 + a15: dgrad GEMMs
   const void* sab = SV + F.sv_ab;
-  switch (p.block_m) {
-    case 32: routed_dgrad<T, Cfg32>(p, w, r, sab, dY, dAB, dXs, s); break;
-    case 64: routed_dgrad<T, Cfg64>(p, w, r, sab, dY, dAB, dXs, s); break;
-    default: routed_dgrad<T, Cfg128>(p, w, r, sab, dY, dAB, dXs, s); break;
-  }
+  routed_dgrad<T>(p, w, r, sab, dY, dAB, dXs, s);
   // a14: per-expert weight gradients, K = the expert's rows
   {
     WgradArgs a{};
@@ -369,7 +394,6 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   if (hs > 0) {
     T* dABs = reinterpret_cast<T*>(W + L.dABs);
     dxs = reinterpret_cast<T*>(W + L.dxs);
-    const int64_t row_tiles = (T_ + Cfg128::BM - 1) / Cfg128::BM;
     const T* ssab = reinterpret_cast<const T*>(SV + F.sv_sab);
     GemmArgs a{};
     a.a = grad_out;
@@ -384,7 +408,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     a.sa = const_cast<T*>(ssab);
     a.sb = const_cast<T*>(ssab + hs);
     a.lds = 2 * static_cast<int64_t>(hs);
-    gemm<T, Cfg128, false, kEpiSwigluBwd, true>("bwd_shared_down_dgrad", a, row_tiles, s);
+    dense_gemm<T, kEpiSwigluBwd>("bwd_shared_down_dgrad", a, s);
     GemmArgs b{};
     b.a = dABs;
     b.lda = 2 * static_cast<int64_t>(hs);
@@ -397,7 +421,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     b.M = T_;
     b.c = dxs;
     b.ldc = d;
-    gemm<T, Cfg128, false, kEpiStore, true>("bwd_shared_gate_up_dgrad", b, row_tiles, s);
+    dense_gemm<T, kEpiStore>("bwd_shared_gate_up_dgrad", b, s);
 
     float* p1 = reinterpret_cast<float*>(W + L.part_sd);
     WgradArgs c{};

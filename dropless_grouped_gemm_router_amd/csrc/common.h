@@ -14,6 +14,9 @@ typedef uint16_t bf16_t;  // bf16 bit pattern
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+// 16 bytes as a native vector (plain loads/stores and SSA values; HIP's
+// uint4 is a struct whose copies can turn into memcpy).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
@@ -87,6 +90,10 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workgroups of `kernel` (block size `threads`) the current device keeps
+// resident at once: CUs x workgroups per CU (cached per device and kernel).
+int persistent_slots(const void* kernel, int threads);
 
 // Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).
 void trace_push(hipStream_t s, const char* name);

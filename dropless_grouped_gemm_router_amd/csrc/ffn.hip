@@ -63,12 +63,41 @@ void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc
 
 template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
 void gemm(const char* name, const GemmArgs& a, int64_t row_tiles, hipStream_t s) {
+  if (kDense) row_tiles = (a.M + Cfg::BM - 1) / Cfg::BM;
   if (row_tiles <= 0) return;
-  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), gemm_grid<Cfg>(row_tiles, a.N),
-             dim3(256), 0, s, a);
+  const int64_t work = row_tiles * (a.N / Cfg::BN);
+  const int slots = persistent_slots(
+      reinterpret_cast<const void*>(&gemm_kernel<T, Cfg, kGather, kEpi, kDense>), Cfg::NT);
+  const unsigned grid = static_cast<unsigned>(work < slots ? work : slots);
+  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), dim3(grid), dim3(Cfg::NT), 0, s,
+             a, static_cast<int>(work));
 }
 
-template <typename T, typename Cfg>
+// Grouped GEMM over the block_m tile list: the eight-wave 256-column tile
+// when N allows it, else the four-wave 128-column tile.
+template <typename T, bool kGather, int kEpi>
+void grouped_gemm(const char* name, const GemmArgs& a, int bm, int64_t max_tiles, hipStream_t s) {
+  const bool wide = a.N % 256 == 0;
+  if (bm == 128) {
+    if (wide) gemm<T, Cfg128W, kGather, kEpi, false>(name, a, max_tiles, s);
+    else gemm<T, Cfg128, kGather, kEpi, false>(name, a, max_tiles, s);
+  } else if (bm == 64) {
+    if (wide) gemm<T, Cfg64W, kGather, kEpi, false>(name, a, max_tiles, s);
+    else gemm<T, Cfg64, kGather, kEpi, false>(name, a, max_tiles, s);
+  } else {
+    gemm<T, Cfg32, kGather, kEpi, false>(name, a, max_tiles, s);
+  }
+}
+
+// Dense GEMM over all rows (shared expert).
+template <typename T, int kEpi>
+void dense_gemm(const char* name, const GemmArgs& a, hipStream_t s) {
+  if (a.N % 256 == 0) gemm<T, Cfg128W, false, kEpi, true>(name, a, 1, s);
+  else gemm<T, Cfg128, false, kEpi, true>(name, a, 1, s);
+}
+
+
+template <typename T>
 void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const void* gu,
                 const void* dn, void* h_sorted, void* y_sorted, void* sa, void* sb,
                 hipStream_t s) {
@@ -90,7 +119,7 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   a.sa = sa;
   a.sb = sb;
   a.lds = 2 * static_cast<int64_t>(p.d_hidden);
-  gemm<T, Cfg, true, kEpiSwiglu, false>("gemm_gate_up", a, max_tiles, s);
+  grouped_gemm<T, true, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
 
   GemmArgs b{};
   b.a = h_sorted;
@@ -103,13 +132,12 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   b.num_tiles = r.num_tiles;
   b.c = y_sorted;
   b.ldc = p.d_model;
-  gemm<T, Cfg, false, kEpiStore, false>("gemm_down", b, max_tiles, s);
+  grouped_gemm<T, false, kEpiStore>("gemm_down", b, p.block_m, max_tiles, s);
 }
 
 template <typename T>
 void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void* sdn, void* hs,
                 void* out, void* sa, void* sb, hipStream_t s) {
-  const int64_t row_tiles = (p.tokens + Cfg128::BM - 1) / Cfg128::BM;
   GemmArgs a{};
   a.a = x;
   a.lda = p.d_model;
@@ -122,7 +150,7 @@ void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void
   a.sa = sa;
   a.sb = sb;
   a.lds = 2 * static_cast<int64_t>(p.d_shared);
-  gemm<T, Cfg128, false, kEpiSwiglu, true>("shared_gate_up", a, row_tiles, s);
+  dense_gemm<T, kEpiSwiglu>("shared_gate_up", a, s);
 
   GemmArgs b{};
   b.a = hs;
@@ -133,7 +161,7 @@ void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void
   b.M = p.tokens;
   b.c = out;
   b.ldc = p.d_model;
-  gemm<T, Cfg128, false, kEpiStore, true>("shared_down", b, row_tiles, s);
+  dense_gemm<T, kEpiStore>("shared_down", b, s);
 }
 
 template <typename T>
@@ -153,17 +181,7 @@ hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
   T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
-  switch (p.block_m) {
-    case 32:
-      routed_ffn<T, Cfg32>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
-      break;
-    case 64:
-      routed_ffn<T, Cfg64>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
-      break;
-    default:
-      routed_ffn<T, Cfg128>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
-      break;
-  }
+  routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
   if (hs > 0) {
     T* hsb = saved ? reinterpret_cast<T*>(SV + L.sv_sh) : reinterpret_cast<T*>(W + L.h_shared);
     T* ssa = saved ? reinterpret_cast<T*>(SV + L.sv_sab) : nullptr;

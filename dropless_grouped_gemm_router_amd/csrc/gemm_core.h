@@ -54,17 +54,24 @@ struct GemmArgs {
   int hsplit;               // SwiGLU backward: column offset of the up gradient in c
 };
 
-template <int BM_, int WAVES_M_, int WAVES_N_, int WM_SUB_, int WN_SUB_>
+template <int BM_, int WAVES_M_, int WAVES_N_, int WM_SUB_, int WN_SUB_, int WPE_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WPE = WPE_;  // waves per SIMD the register budget is sized for
   static constexpr int WM_SUB = WM_SUB_, WN_SUB = WN_SUB_;
   static constexpr int BN = WAVES_N * WN_SUB * 32;
-  static_assert(WAVES_M * WAVES_N == 4, "four waves");
+  static constexpr int NT = 64 * WAVES_M * WAVES_N;  // threads per workgroup
   static_assert(WAVES_M * WM_SUB * 32 == BM, "rows");
+  static_assert((BM * 8) % NT == 0 && (BN * 8) % NT == 0, "whole chunks per thread");
 };
-using Cfg128 = TileCfg<128, 2, 2, 2, 2>;  // BN 128
-using Cfg64 = TileCfg<64, 2, 2, 1, 2>;    // BN 128
-using Cfg32 = TileCfg<32, 1, 4, 1, 1>;    // BN 128
+// Four-wave tiles (BN 128), one per block_m.
+using Cfg128 = TileCfg<128, 2, 2, 2, 2>;
+using Cfg64 = TileCfg<64, 2, 2, 1, 2>;
+using Cfg32 = TileCfg<32, 1, 4, 1, 1>;
+// Eight-wave tiles with BN 256: twice the MFMA work per byte staged. Wide
+// N (a whole gate|up block of width <= 128, or 256 model columns) per tile.
+using Cfg128W = TileCfg<128, 2, 4, 2, 2>;  // 128 x 256, waves 64 x 64
+using Cfg64W = TileCfg<64, 2, 4, 1, 2>;    // 64 x 256, waves 32 x 64
 
 constexpr int kStageBytes = 128;   // K bytes per row per stage
 constexpr int kLdsRowBytes = 144;  // + 16 bytes padding
@@ -74,7 +81,7 @@ struct Mfma;
 template <>
 struct Mfma<bf16_t> {
   // One 16-byte chunk per lane group: 32x32x16.
-  __device__ static void step(const uint4& w, const uint4& x, f32x16_t& acc) {
+  __device__ static void step(const u32x4& w, const u32x4& x, f32x16_t& acc) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w),
                                                   __builtin_bit_cast(bf16x8_t, x), acc, 0, 0, 0);
   }
@@ -83,7 +90,7 @@ template <>
 struct Mfma<float> {
   // One 16-byte chunk per lane group = 4 k values: four 32x32x2 steps, step s
   // taking element s of each lane group's chunk (the same k on both sides).
-  __device__ static void step(const uint4& w, const uint4& x, f32x16_t& acc) {
+  __device__ static void step(const u32x4& w, const u32x4& x, f32x16_t& acc) {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(w.x), __uint_as_float(x.x), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(w.y), __uint_as_float(x.y), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(w.z), __uint_as_float(x.z), acc, 0, 0, 0);
@@ -91,26 +98,38 @@ struct Mfma<float> {
   }
 };
 
-// Pipeline pieces of the GEMM main loop (force-inlined so that the staging
-// registers stay in VGPRs).
+// Pipeline pieces of the GEMM main loop. A stage's staging registers travel
+// by value so they stay in VGPRs.
 template <int A_CH, int B_CH>
-__device__ __forceinline__ void gemm_gload(uint4 (&ra)[A_CH], uint4 (&rb)[B_CH],
-                                           const char* const (&a_src)[A_CH], const char* b_base,
-                                           const int (&b_off)[B_CH], int off) {
+struct StageRegs {
+  u32x4 a[A_CH];
+  u32x4 b[B_CH];
+};
+
+template <int A_CH, int B_CH, int NT>
+__device__ __forceinline__ StageRegs<A_CH, B_CH> gemm_gload(const char* const (&a_src)[A_CH],
+                                                           const char* b_src, int64_t b_row_bytes,
+                                                           int off) {
+  StageRegs<A_CH, B_CH> r;
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + off);
+  for (int i = 0; i < A_CH; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(a_src[i] + off);
+  // b_src already points at this thread's first chunk; chunk i is NT/8 rows further.
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_base + b_off[i] + off);
+  for (int i = 0; i < B_CH; ++i)
+    r.b[i] = *reinterpret_cast<const u32x4*>(b_src + i * (NT / 8) * b_row_bytes + off);
+  return r;
 }
 
-template <int A_CH, int B_CH>
-__device__ __forceinline__ void gemm_lstore(char* s, const uint4 (&ra)[A_CH],
-                                            const uint4 (&rb)[B_CH], const int (&a_dst)[A_CH],
-                                            const int (&b_dst)[B_CH]) {
+// Thread tid stages 16-byte chunk (tid + NT i) of each operand tile: row
+// (tid >> 3) + (NT / 8) i, column chunk tid & 7.
+template <int A_CH, int B_CH, int A_BYTES, int NT>
+__device__ __forceinline__ void gemm_lstore(char* s, const StageRegs<A_CH, B_CH> r, int lds_off) {
 #pragma unroll
-  for (int i = 0; i < A_CH; ++i) *reinterpret_cast<uint4*>(s + a_dst[i]) = ra[i];
+  for (int i = 0; i < A_CH; ++i)
+    *reinterpret_cast<u32x4*>(s + lds_off + i * (NT / 8) * kLdsRowBytes) = r.a[i];
 #pragma unroll
-  for (int i = 0; i < B_CH; ++i) *reinterpret_cast<uint4*>(s + b_dst[i]) = rb[i];
+  for (int i = 0; i < B_CH; ++i)
+    *reinterpret_cast<u32x4*>(s + A_BYTES + lds_off + i * (NT / 8) * kLdsRowBytes) = r.b[i];
 }
 
 // One K stage out of LDS: four fragment steps of 32 bytes per row.
@@ -119,13 +138,13 @@ __device__ __forceinline__ void gemm_compute(const char* s, int a_frag, int b_fr
                                              f32x16_t (&acc)[WM_SUB][WN_SUB]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    uint4 xf[WM_SUB], wf[WN_SUB];
+    u32x4 xf[WM_SUB], wf[WN_SUB];
 #pragma unroll
     for (int i = 0; i < WM_SUB; ++i)
-      xf[i] = *reinterpret_cast<const uint4*>(s + a_frag + i * 32 * kLdsRowBytes + q * 32);
+      xf[i] = *reinterpret_cast<const u32x4*>(s + a_frag + i * 32 * kLdsRowBytes + q * 32);
 #pragma unroll
     for (int j = 0; j < WN_SUB; ++j)
-      wf[j] = *reinterpret_cast<const uint4*>(s + b_frag + j * 32 * kLdsRowBytes + q * 32);
+      wf[j] = *reinterpret_cast<const u32x4*>(s + b_frag + j * 32 * kLdsRowBytes + q * 32);
 #pragma unroll
     for (int i = 0; i < WM_SUB; ++i)
 #pragma unroll
@@ -133,102 +152,15 @@ __device__ __forceinline__ void gemm_compute(const char* s, int a_frag, int b_fr
   }
 }
 
-template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
-__global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs p) {
-  constexpr int BM = Cfg::BM, BN = Cfg::BN;
-  constexpr int WM_SUB = Cfg::WM_SUB, WN_SUB = Cfg::WN_SUB;
-  constexpr int A_CH = BM * 8 / 256;  // 16-byte chunks per thread per stage
-  constexpr int B_CH = BN * 8 / 256;
-  constexpr int KT = kStageBytes / static_cast<int>(sizeof(T));
-  constexpr int A_BYTES = BM * kLdsRowBytes, B_BYTES = BN * kLdsRowBytes;
-  __shared__ __attribute__((aligned(16))) char smem[2 * (A_BYTES + B_BYTES)];
-
-  const int n_tiles_n = p.N / BN;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int mt = logical / n_tiles_n, nt = logical % n_tiles_n;
-  int group, row0, rows;
-  if (kDense) {
-    group = 0;
-    row0 = mt * BM;
-    if (row0 >= p.M) return;
-    rows = static_cast<int>(min(static_cast<int64_t>(BM), p.M - row0));
-  } else {
-    if (mt >= *p.num_tiles) return;
-    group = p.tiles[3 * mt + 0];
-    row0 = p.tiles[3 * mt + 1];
-    rows = p.tiles[3 * mt + 2];
-  }
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 5, r32 = lane & 31;
-  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
-
-  // Global source of each chunk this thread stages (rows past the tile's end
-  // re-read its last row; their results are never stored).
-  const char* a_src[A_CH];
-  int a_dst[A_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * 256;
-    const int r = c >> 3, c16 = c & 7;
-    const int mr = min(r, rows - 1);
-    int64_t src_row;
-    if (kGather) src_row = p.perm[row0 + mr] / p.topk;
-    else src_row = static_cast<int64_t>(row0) + mr;
-    a_src[i] = static_cast<const char*>(p.a) + (src_row * p.lda) * static_cast<int64_t>(sizeof(T)) + c16 * 16;
-    a_dst[i] = r * kLdsRowBytes + c16 * 16;
-  }
-  const int64_t ldb = p.ldb ? p.ldb : p.K;
-  const char* b_base = static_cast<const char*>(p.b) +
-                       (static_cast<int64_t>(group) * p.b_group_stride +
-                        static_cast<int64_t>(nt) * BN * ldb) * static_cast<int64_t>(sizeof(T));
-  const char* b2_base = p.b2 ? static_cast<const char*>(p.b2) +
-                                   (static_cast<int64_t>(group) * p.b2_group_stride +
-                                    static_cast<int64_t>(nt) * BN * ldb -
-                                    static_cast<int64_t>(p.ksplit)) * static_cast<int64_t>(sizeof(T))
-                             : nullptr;
-  const int ks_split = p.b2 ? p.ksplit / KT : (1 << 30);  // first stage read from b2
-  int b_off[B_CH];
-  int b_dst[B_CH];
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * 256;
-    const int r = c >> 3, c16 = c & 7;
-    b_off[i] = static_cast<int>(r * ldb * static_cast<int64_t>(sizeof(T))) + c16 * 16;
-    b_dst[i] = A_BYTES + r * kLdsRowBytes + c16 * 16;
-  }
-
-  f32x16_t acc[WM_SUB][WN_SUB];
-#pragma unroll
-  for (int i = 0; i < WM_SUB; ++i)
-#pragma unroll
-    for (int j = 0; j < WN_SUB; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-  const int nk = p.K / KT;
-  const int a_frag = (wm * WM_SUB * 32 + r32) * kLdsRowBytes + g * 16;
-  const int b_frag = A_BYTES + (wn * WN_SUB * 32 + r32) * kLdsRowBytes + g * 16;
-  uint4 ra[A_CH], rb[B_CH];
-  gemm_gload<A_CH, B_CH>(ra, rb, a_src, b_base, b_off, 0);
-  gemm_lstore<A_CH, B_CH>(smem, ra, rb, a_dst, b_dst);
-  __syncthreads();
-  // Software pipeline: stage ks+1 is fetched into registers while stage ks
-  // is multiplied out of LDS; the last stage is peeled.
-  for (int ks = 0; ks + 1 < nk; ++ks) {
-    const int buf = ks & 1;
-    gemm_gload<A_CH, B_CH>(ra, rb, a_src, ks + 1 < ks_split ? b_base : b2_base, b_off,
-                           (ks + 1) * kStageBytes);
-    gemm_compute<T, WM_SUB, WN_SUB>(smem + buf * (A_BYTES + B_BYTES), a_frag, b_frag, acc);
-    gemm_lstore<A_CH, B_CH>(smem + (buf ^ 1) * (A_BYTES + B_BYTES), ra, rb, a_dst, b_dst);
-    __syncthreads();
-  }
-  gemm_compute<T, WM_SUB, WN_SUB>(smem + ((nk - 1) & 1) * (A_BYTES + B_BYTES), a_frag, b_frag, acc);
-
-  // Epilogue. Accumulator register q of MFMA tile (i, j) holds row
-  // m = i*32 + r32 and column n = j*32 + 8*(q/4) + 4*g + q%4 of the wave's
-  // sub-block.
+// Epilogue of one tile. Accumulator register q of MFMA tile (i, j) holds row
+// m = i*32 + r32 and column n = j*32 + 8*(q/4) + 4*g + q%4 of the wave's
+// sub-block, so each lane writes runs of four consecutive columns.
+template <typename T, typename Cfg, int kEpi>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p,
+                                              const f32x16_t (&acc)[Cfg::WM_SUB][Cfg::WN_SUB],
+                                              int row0, int rows, int nt, int wm, int wn, int g,
+                                              int r32) {
+  constexpr int WM_SUB = Cfg::WM_SUB, WN_SUB = Cfg::WN_SUB, BN = Cfg::BN;
   T* c = static_cast<T*>(p.c);
 #pragma unroll
   for (int i = 0; i < WM_SUB; ++i) {
@@ -289,6 +221,182 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(const GemmArgs p) {
   }
 }
 
+// Row tile of one work item: its weight group, first output row and rows.
+struct TileInfo {
+  int group, row0, rows;
+};
+
+template <typename Cfg, bool kDense>
+__device__ __forceinline__ TileInfo tile_info(const GemmArgs& p, int w, int n_tiles_n) {
+  const int mt = w / n_tiles_n;
+  TileInfo t;
+  if (kDense) {
+    t.group = 0;
+    t.row0 = mt * Cfg::BM;
+    const int64_t left = p.M - t.row0;
+    t.rows = left <= 0 ? 0 : static_cast<int>(left < Cfg::BM ? left : Cfg::BM);
+  } else if (mt < *p.num_tiles) {
+    t.group = p.tiles[3 * mt + 0];
+    t.row0 = p.tiles[3 * mt + 1];
+    t.rows = p.tiles[3 * mt + 2];
+  } else {
+    t.group = 0;
+    t.row0 = 0;
+    t.rows = 0;  // past the last tile
+  }
+  return t;
+}
+
+// Source rows of the A chunks this thread stages for a tile (rows past the
+// tile's end repeat its last row; their results are never stored).
+template <int A_CH, int NT, bool kGather>
+__device__ __forceinline__ void tile_rows(const GemmArgs& p, const TileInfo& t, int tid,
+                                          int (&src)[A_CH]) {
+#pragma unroll
+  for (int i = 0; i < A_CH; ++i) {
+    const int r = (tid + i * NT) >> 3;
+    const int mr = t.rows > 0 ? min(r, t.rows - 1) : 0;
+    src[i] = kGather ? (t.rows > 0 ? p.perm[t.row0 + mr] / p.topk : 0) : t.row0 + mr;
+  }
+}
+
+// Persistent grouped GEMM. Workgroup b runs on XCD b % 8 (round-robin
+// dispatch) and walks that XCD's contiguous share of the (row tile, N tile)
+// work list, so the tiles of one expert, and its weights, stay in one L2.
+// The next item's metadata is fetched at the start of a tile and its
+// gathered row indices before this tile's epilogue, off the critical path.
+template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(Cfg::WPE)))
+void gemm_kernel(const GemmArgs p, int total_work) {
+  constexpr int BM = Cfg::BM, BN = Cfg::BN, NT = Cfg::NT;
+  constexpr int WM_SUB = Cfg::WM_SUB, WN_SUB = Cfg::WN_SUB;
+  constexpr int A_CH = BM * 8 / NT;  // 16-byte chunks per thread per stage
+  constexpr int B_CH = BN * 8 / NT;
+  constexpr int KT = kStageBytes / static_cast<int>(sizeof(T));
+  constexpr int A_BYTES = BM * kLdsRowBytes, B_BYTES = BN * kLdsRowBytes;
+  __shared__ __attribute__((aligned(16))) char smem[2 * (A_BYTES + B_BYTES)];
+
+  const int n_tiles_n = p.N / BN;
+  const int G = gridDim.x;
+  const int nx = G < 8 ? G : 8;
+  const int x = blockIdx.x % nx, wi = blockIdx.x / nx;
+  const int gx = G / nx + (x < G % nx ? 1 : 0);
+  const int per = (total_work + nx - 1) / nx;
+  const int w_end = min(total_work, (x + 1) * per);
+  int w = x * per + wi;
+  if (w >= w_end) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
+  const int64_t ldb = p.ldb ? p.ldb : p.K;
+  const int ks_split = p.b2 ? p.ksplit / KT : (1 << 30);  // first stage read from b2
+  const int nk = p.K / KT;
+  const int a_frag = (wm * WM_SUB * 32 + r32) * kLdsRowBytes + g * 16;
+  const int b_frag = A_BYTES + (wn * WN_SUB * 32 + r32) * kLdsRowBytes + g * 16;
+  const int bufb = A_BYTES + B_BYTES;
+  const int lds_off = (tid >> 3) * kLdsRowBytes + (tid & 7) * 16;
+  const int64_t b_row_bytes = ldb * static_cast<int64_t>(sizeof(T));
+  const int64_t b_thr = (tid >> 3) * b_row_bytes + (tid & 7) * 16;
+
+  TileInfo cur = tile_info<Cfg, kDense>(p, w, n_tiles_n);
+  int src_cur[A_CH];
+  tile_rows<A_CH, NT, kGather>(p, cur, tid, src_cur);
+
+  while (true) {
+    if (cur.rows <= 0) break;  // past the last tile; every later item is too
+    const int nt = w % n_tiles_n;
+    const int group = cur.group, row0 = cur.row0, rows = cur.rows;
+    const char* a_src[A_CH];
+#pragma unroll
+    for (int i = 0; i < A_CH; ++i)
+      a_src[i] = static_cast<const char*>(p.a) +
+                 static_cast<int64_t>(src_cur[i]) * p.lda * static_cast<int64_t>(sizeof(T)) +
+                 ((tid + i * NT) & 7) * 16;
+    const char* b_base = static_cast<const char*>(p.b) + b_thr +
+                         (static_cast<int64_t>(group) * p.b_group_stride +
+                          static_cast<int64_t>(nt) * BN * ldb) * static_cast<int64_t>(sizeof(T));
+    const char* b2_base = p.b2 ? static_cast<const char*>(p.b2) + b_thr +
+                                     (static_cast<int64_t>(group) * p.b2_group_stride +
+                                      static_cast<int64_t>(nt) * BN * ldb -
+                                      static_cast<int64_t>(p.ksplit)) * static_cast<int64_t>(sizeof(T))
+                               : nullptr;
+    auto stage_b = [&](int st) { return st < ks_split ? b_base : b2_base; };
+
+    StageRegs<A_CH, B_CH> r0 = gemm_gload<A_CH, B_CH, NT>(a_src, b_base, b_row_bytes, 0);
+    StageRegs<A_CH, B_CH> r1 = r0;
+    if (nk > 1) r1 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(1), b_row_bytes, kStageBytes);
+    // Metadata of the next item (its row indices are fetched after this tile).
+    const int w1 = w + gx;
+    const TileInfo nxt = (w1 < w_end) ? tile_info<Cfg, kDense>(p, w1, n_tiles_n) : TileInfo{0, 0, 0};
+
+    f32x16_t acc[WM_SUB][WN_SUB];
+#pragma unroll
+    for (int i = 0; i < WM_SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < WN_SUB; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem, r0, lds_off);
+    __syncthreads();
+    // Steady state (no branches): LDS buffer s&1 holds stage s, one register
+    // set holds stage s+1 and the other receives stage s+2. The scheduling
+    // fences keep that order: loads issue before the MFMAs and the LDS
+    // store (which waits for its loads) comes after them; left alone, the
+    // compiler hoists the store and sinks the loads to save registers,
+    // which shortens the prefetch distance to under one stage.
+    int s = 0;
+    for (; s + 3 < nk; s += 2) {
+      r0 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + 2), b_row_bytes, (s + 2) * kStageBytes);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, r1, lds_off);
+      __syncthreads();
+      r1 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + 3), b_row_bytes, (s + 3) * kStageBytes);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + ((s + 1) & 1) * bufb, a_frag, b_frag, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + (s & 1) * bufb, r0, lds_off);
+      __syncthreads();
+    }
+    // Tail: one to three stages remain (s in LDS, s+1 in r1).
+    if (s + 2 < nk) {
+      r0 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + 2), b_row_bytes, (s + 2) * kStageBytes);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, r1, lds_off);
+      __syncthreads();
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + ((s + 1) & 1) * bufb, a_frag, b_frag, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + (s & 1) * bufb, r0, lds_off);
+      __syncthreads();
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+    } else if (s + 1 < nk) {
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, r1, lds_off);
+      __syncthreads();
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + ((s + 1) & 1) * bufb, a_frag, b_frag, acc);
+    } else {
+      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+    }
+    // Row indices of the next item, while this tile's results drain.
+    tile_rows<A_CH, NT, kGather>(p, nxt, tid, src_cur);
+
+    gemm_epilogue<T, Cfg, kEpi>(p, acc, row0, rows, nt, wm, wn, g, r32);
+
+    // The last stage's LDS reads finish before the next tile's first store.
+    __syncthreads();
+    w += gx;
+    if (w >= w_end) break;
+    cur = nxt;
+  }
+}
+
 // ------------------------------------------------------------------ wgrad
 // Weight-gradient GEMM: the reduction runs over token rows.
 //
@@ -328,7 +436,7 @@ template <>
 struct Transpose<bf16_t> {
   static constexpr int V = 8;
   // out[c] = (in[0][c], in[1][c], ..., in[7][c])
-  __device__ static void run(const uint4* in, uint4* out) {
+  __device__ static void run(const u32x4* in, u32x4* out) {
     const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[4*r + c/2]
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -338,18 +446,18 @@ struct Transpose<bf16_t> {
         const uint32_t lo = w[4 * (2 * q) + c / 2], hi = w[4 * (2 * q + 1) + c / 2];
         o[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
       }
-      out[c] = make_uint4(o[0], o[1], o[2], o[3]);
+      out[c] = (u32x4){o[0], o[1], o[2], o[3]};
     }
   }
 };
 template <>
 struct Transpose<float> {
   static constexpr int V = 4;
-  __device__ static void run(const uint4* in, uint4* out) {
-    out[0] = make_uint4(in[0].x, in[1].x, in[2].x, in[3].x);
-    out[1] = make_uint4(in[0].y, in[1].y, in[2].y, in[3].y);
-    out[2] = make_uint4(in[0].z, in[1].z, in[2].z, in[3].z);
-    out[3] = make_uint4(in[0].w, in[1].w, in[2].w, in[3].w);
+  __device__ static void run(const u32x4* in, u32x4* out) {
+    out[0] = (u32x4){in[0].x, in[1].x, in[2].x, in[3].x};
+    out[1] = (u32x4){in[0].y, in[1].y, in[2].y, in[3].y};
+    out[2] = (u32x4){in[0].z, in[1].z, in[2].z, in[3].z};
+    out[3] = (u32x4){in[0].w, in[1].w, in[2].w, in[3].w};
   }
 };
 
@@ -357,7 +465,7 @@ struct Transpose<float> {
 // V x V blocks of A (blocks 0 .. NB-1) and B (NB .. 2NB-1); rows outside
 // [r0, r1) read as zeros.
 template <typename T, bool kGatherA, int PER, int V, int NB, int KT>
-__device__ __forceinline__ void wgrad_gload(const WgradArgs& p, uint4 (&blk)[PER][V], int64_t r0,
+__device__ __forceinline__ void wgrad_gload(const WgradArgs& p, u32x4 (&blk)[PER][V], int64_t r0,
                                             int64_t r1, int ks, int mt, int nt, int tid) {
   constexpr int CB = 128 / V;  // column blocks per operand row
 #pragma unroll
@@ -369,7 +477,7 @@ __device__ __forceinline__ void wgrad_gload(const WgradArgs& p, uint4 (&blk)[PER
 #pragma unroll
     for (int rr = 0; rr < V; ++rr) {
       const int64_t r = r0 + static_cast<int64_t>(ks) * KT + rb * V + rr;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
       if (r < r1) {
         const T* src;
         if (is_b) {
@@ -378,7 +486,7 @@ __device__ __forceinline__ void wgrad_gload(const WgradArgs& p, uint4 (&blk)[PER
           const int64_t ar = kGatherA ? static_cast<int64_t>(p.perm[r] / p.topk) : r;
           src = static_cast<const T*>(p.a) + ar * p.lda + mt * 128 + cb * V;
         }
-        v = *reinterpret_cast<const uint4*>(src);
+        v = *reinterpret_cast<const u32x4*>(src);
       }
       blk[q][rr] = v;
     }
@@ -387,7 +495,7 @@ __device__ __forceinline__ void wgrad_gload(const WgradArgs& p, uint4 (&blk)[PER
 
 // Transposes the fetched blocks into K-contiguous LDS rows.
 template <typename T, int PER, int V, int NB, int A_BYTES>
-__device__ __forceinline__ void wgrad_lstore(char* s, const uint4 (&blk)[PER][V], int tid) {
+__device__ __forceinline__ void wgrad_lstore(char* s, const u32x4 (&blk)[PER][V], int tid) {
   constexpr int CB = 128 / V;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
@@ -395,11 +503,11 @@ __device__ __forceinline__ void wgrad_lstore(char* s, const uint4 (&blk)[PER][V]
     const bool is_b = b >= NB;
     const int bb = is_b ? b - NB : b;
     const int rb = bb / CB, cb = bb % CB;
-    uint4 t[V];
+    u32x4 t[V];
     Transpose<T>::run(blk[q], t);
     char* base = s + (is_b ? A_BYTES : 0) + rb * 16;
 #pragma unroll
-    for (int cc = 0; cc < V; ++cc) *reinterpret_cast<uint4*>(base + (cb * V + cc) * kLdsRowBytes) = t[cc];
+    for (int cc = 0; cc < V; ++cc) *reinterpret_cast<u32x4*>(base + (cb * V + cc) * kLdsRowBytes) = t[cc];
   }
 }
 
@@ -442,7 +550,7 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const WgradArgs p) {
   const int nk = static_cast<int>((r1 - r0 + KT - 1) / KT);
   const int a_frag = (wm * WM_SUB * 32 + r32) * kLdsRowBytes + g * 16;
   const int b_frag = A_BYTES + (wn * WN_SUB * 32 + r32) * kLdsRowBytes + g * 16;
-  uint4 blk[PER][V];
+  u32x4 blk[PER][V];
   if (nk > 0) {
     wgrad_gload<T, kGatherA, PER, V, NB, KT>(p, blk, r0, r1, 0, mt, nt, tid);
     wgrad_lstore<T, PER, V, NB, A_BYTES>(smem, blk, tid);
