@@ -5,11 +5,14 @@ tokens: route -> permute -> grouped gated FFN (+ shared expert) -> combine,
 all through the libmoe C ABI on the current stream. Inputs and weights are
 resident in HBM before timing starts.
 
-Prints one JSON line (tokens/s, per-kernel times, the dominant kernel's
-roofline fraction and the CPU oracle's throughput on a bounded sample).
+Prints one JSON line: tokens/s, per-kernel times from HIP events over the
+timed steps, the dominant kernel's roofline fraction, the train step
+(forward + backward) on the 16384-token workload, and the CPU oracle's
+throughput on a bounded sample of the same workload.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -18,47 +21,174 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# MI355X published dense peaks.
+# MI355X published dense peaks (no sparsity).
 PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# fp32 vector FMA peak without packed math: 256 CUs x 64 lanes x 2 flop x 2.4 GHz.
+PEAK_VALU_TFLOPS = 78.6
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["gemm_core.h", "ffn.hip", "route.hip", "permute.hip", "combine.hip", "common.h"]
 
 
-def flops(p):
-    """Algorithmic FLOPs of one forward, per kernel (multiply-add = 2)."""
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def work(p):
+    """Algorithmic work of each forward kernel per launch: (kind, amount).
+    FLOPs count a multiply-add as 2; bytes are the minimum each kernel must
+    move (inputs read once, outputs written once)."""
     T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
     S = T * k
-    f = {
-        "route": 2 * T * d * E,
-        "gemm_gate_up": 2 * S * d * 2 * h,
-        "gemm_down": 2 * S * h * d,
+    es = 2 if p.dtype == "bf16" else 4
+    w = {
+        "route": ("flop", 2 * T * d * E),
+        "gemm_gate_up": ("flop", 2 * S * d * 2 * h),
+        "gemm_down": ("flop", 2 * S * h * d),
+        # y_sorted and shared_out read, combine weights and slot map read, out written
+        "combine": ("byte", S * d * es + S * 8 + T * d * es * (2 if hs else 1)),
+        # expert indices read twice (count, scatter), perm and inv_perm written
+        "permute_scatter": ("byte", S * 4 * 3),
     }
     if hs:
-        f["shared_gate_up"] = 2 * T * d * 2 * hs
-        f["shared_down"] = 2 * T * hs * d
-    return f
+        w["shared_gate_up"] = ("flop", 2 * T * d * 2 * hs)
+        w["shared_down"] = ("flop", 2 * T * hs * d)
+    return w
 
 
-def cpu_baseline(p, sample_tokens):
+def roofline_of(kname, kind, amount, avg_ms, dtype):
+    if kind == "byte":
+        ach = amount / (avg_ms * 1e-3) / 1e9
+        return {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
+    ach = amount / (avg_ms * 1e-3) / 1e12
+    if kname == "route":
+        return {"kernel": kname, "bound": "alu", "achieved": ach, "peak": PEAK_VALU_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_VALU_TFLOPS}
+    peak = PEAK_TFLOPS[dtype]
+    return {"kernel": kname, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+            "frac": ach / peak}
+
+
+def trace_name(kernel):
+    """libmoe trace name of a compiled forward kernel, from its signature."""
+    import re
+    if "route_kernel" in kernel:
+        return "route"
+    if "combine_kernel" in kernel:
+        return "combine"
+    for k in ("count", "scan", "scatter"):
+        if f"{k}_kernel" in kernel:
+            return f"permute_{k}"
+    if "pack_kernel" in kernel:
+        return "pack_weights"
+    m = re.search(r"gemm_kernel<[^>]*>, (true|false), (\d), (true|false)>", kernel)
+    if m:
+        gather, epi, dense = m.group(1) == "true", int(m.group(2)), m.group(3) == "true"
+        if dense:
+            return "shared_gate_up" if epi == 1 else "shared_down"
+        return "gemm_gate_up" if epi == 1 else "gemm_down"
+    return None
+
+
+def pmc_summary(fetch_dir, write_dir, copyf_dir, copyw_dir, workload_name, out_path):
+    """HBM bytes per launch of each forward kernel from rocprofv3 FETCH_SIZE
+    and WRITE_SIZE runs (KiB per dispatch), each scaled by what the same
+    counter reports for a plain device copy of known size."""
+    import csv
+    import statistics
+
+    def per_kernel(d, counter):
+        vals = {}
+        with open(os.path.join(d, "run_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    def copy_scale(d, counter):
+        vals = per_kernel(d, counter)
+        kib = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        n = 1024 << 20  # the calibration copies 1024 MiB
+        return n / (statistics.median(kib) * 1024.0)
+
+    fs, ws = copy_scale(copyf_dir, "FETCH_SIZE"), copy_scale(copyw_dir, "WRITE_SIZE")
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    out = {"workload": workload_name, "source_hash": kernel_source_hash(),
+           "fetch_scale": fs, "write_scale": ws, "kernels": {}}
+    for k, fv in fetch.items():
+        name = trace_name(k)
+        if name is None or k not in write:
+            continue
+        fb = statistics.median(fv) * 1024.0 * fs
+        wb = statistics.median(write[k]) * 1024.0 * ws
+        out["kernels"][name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    with open(out_path, "w") as fh:
+        json.dump(out, fh, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
+def cpu_baseline(p, inputs, sample_tokens):
     """The CPU oracle (as it stands) on the first `sample_tokens` tokens of
-    the same workload: routing, permutation and every output row."""
-    import dataclasses
-
-    from dropless_grouped_gemm_router_amd.inputs import make_inputs
+    the same generated inputs: routing, permutation and every output row."""
     from oracle import oracle
 
-    q = dataclasses.replace(p, tokens=sample_tokens)
-    inp = make_inputs(q, seed=0)
-    v = {n: t.value for n, t in inp.items()}
+    v = {n: t.value for n, t in inputs.items()}
+    x = v["x"][:sample_tokens]
     nthreads = oracle.max_threads()
     t0 = time.perf_counter()
-    _, idx, w = oracle.route(v["x"], v["w_router"], q.top_k, nthreads)
-    oracle.permute(idx, q.experts, q.block_m)
-    oracle.forward_rows(v["x"], v["w_gate"], v["w_up"], v["w_down"], idx, w, v.get("ws_gate"),
+    _, idx, w = oracle.route(x, v["w_router"], p.top_k, nthreads)
+    oracle.permute(idx, p.experts, p.block_m)
+    oracle.forward_rows(x, v["w_gate"], v["w_up"], v["w_down"], idx, w, v.get("ws_gate"),
                         v.get("ws_up"), v.get("ws_down"), nthreads=nthreads)
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
-            "sample": f"first {sample_tokens} tokens of the same workload (seed 0), full forward "
-                      f"in double, {dt:.1f} s wall"}
+            "sample": f"first {sample_tokens} of the {p.tokens} tokens of the same seeded inputs: "
+                      f"routing, permutation and every output row in double, {dt:.1f} s wall"}
+
+
+def time_steps(step, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def train_step_line(B, steps, warmup):
+    """Forward + backward on the train-step workload (16384 tokens)."""
+    import torch
+
+    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, make_inputs
+
+    name, p, _ = WORKLOADS[4]
+    dev = B.device_inputs(make_inputs(p, seed=0, with_grad_out=True), "cuda:0")
+    buf = B.allocate(p, "cuda:0", training=True)
+    x, g = dev.pop("x"), dev.pop("grad_out")
+    torch.cuda.synchronize()
+
+    def step():
+        B.forward(p, x, dev, buf, training=True)
+        B.backward(p, x, dev, g, buf)
+
+    ms = time_steps(step, steps, warmup)
+    T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
+    fwd = 2 * T * d * E + 6 * T * k * d * h + 6 * T * d * hs
+    return {"workload": name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "tflops_3x_fwd": 3 * fwd / (ms * 1e-3) / 1e12, "steps": steps, "warmup": warmup}
 
 
 def main():
@@ -68,11 +198,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="index into inputs.WORKLOADS")
     ap.add_argument("--block-m", type=int, default=None)
-    ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--cpu-sample", type=int, default=131072,
+                    help="tokens the CPU oracle runs on (about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
+                    help="write profiles/traffic.json from rocprofv3 --pmc output directories")
     args = ap.parse_args()
+    if args.pmc_summary:
+        from dropless_grouped_gemm_router_amd.inputs import WORKLOADS
+        pmc_summary(*args.pmc_summary, WORKLOADS[args.workload][0], TRAFFIC_FILE)
+        return
     if args.calibrate_copy:
         import torch
         n = args.calibrate_copy << 20
@@ -86,7 +224,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
-              "requested); see the sharding paragraph of the design notes.", file=sys.stderr)
+              "requested); the design notes describe how the path would shard.", file=sys.stderr)
         sys.exit(2)
 
     import dataclasses
@@ -101,7 +239,8 @@ def main():
         p = dataclasses.replace(p, block_m=args.block_m)
     torch.cuda.set_device(0)
     print(f"bench: {name} bm={p.block_m}: generating inputs", file=sys.stderr, flush=True)
-    dev = B.device_inputs(make_inputs(p, seed=0), "cuda:0")
+    inputs = make_inputs(p, seed=0)
+    dev = B.device_inputs(inputs, "cuda:0")
     buf = B.allocate(p, "cuda:0")
     x = dev.pop("x")
     w = dev
@@ -114,29 +253,32 @@ def main():
         step()
     torch.cuda.synchronize()
     print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Per-kernel HIP events bracket every launch of the timed steps.
     B.moe_trace_enable(True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = time_steps(step, args.steps, 0)
     kern = B.moe_trace_summary()
     B.moe_trace_enable(False)
 
-    f = flops(p)
-    per = {k: {"ms": v["ms"] / max(1, v["count"]) * (v["count"] / args.steps),
-               "launches_per_step": v["count"] / args.steps} for k, v in kern.items()}
-    gemms = [k for k in f if k != "route" and k in per]
-    dom = max(gemms, key=lambda k: per[k]["ms"])
-    dom_avg_ms = kern[dom]["ms"] / kern[dom]["count"]
-    achieved = f[dom] / (dom_avg_ms * 1e-3) / 1e12
+    wk = work(p)
+    per_step = {k: v["ms"] / args.steps for k, v in kern.items()}
+    avg = {k: v["ms"] / v["count"] for k, v in kern.items()}
+    dom = max(per_step, key=per_step.get)
+    rooflines = {k: roofline_of(k, wk[k][0], wk[k][1], avg[k], p.dtype) for k in wk if k in avg}
+    roof = dict(rooflines[dom]) if dom in rooflines else None
+    if roof is not None:
+        roof["traffic"] = None
+        try:
+            with open(TRAFFIC_FILE) as fh:
+                tr = json.load(fh)
+            ent = tr.get("kernels", {}).get(dom)
+            if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == name:
+                roof["traffic"] = ent["bytes_per_launch"]
+        except (OSError, ValueError):
+            pass
     peak = PEAK_TFLOPS[p.dtype]
-    routed_ms = sum(per[k]["ms"] for k in ("gemm_gate_up", "gemm_down"))
-    routed_fl = f["gemm_gate_up"] + f["gemm_down"]
-    total_fl = sum(f.values())
+    routed_ms = sum(avg[k] for k in ("gemm_gate_up", "gemm_down") if k in avg)
+    routed_fl = wk["gemm_gate_up"][1] + wk["gemm_down"][1]
+    total_fl = sum(v[1] for k, v in wk.items() if v[0] == "flop")
     line = {
         "metric": "dropless MoE fwd tokens/s + grouped-GEMM % MFMA peak (E=64 top-8, 131k tok)",
         "value": p.tokens / (ms * 1e-3),
@@ -149,19 +291,24 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": p.dtype,
-        "data": "synthetic (seeded Gaussian tokens, N(0,1/fan_in) weights)",
+        "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, uniform routing",
         "config": {"workload": name, "tokens": p.tokens, "experts": p.experts, "top_k": p.top_k,
                    "d_model": p.d_model, "d_hidden": p.d_hidden, "d_shared": p.d_shared,
                    "block_m": p.block_m},
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
-        "roofline": {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": peak,
-                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": None},
-        "kernels_ms_per_step": {k: round(v["ms"], 5) for k, v in sorted(per.items())},
+        "roofline": roof,
+        "kernels_ms_per_step": {k: round(v, 5) for k, v in sorted(per_step.items())},
+        "kernel_rooflines": {k: {"frac": round(r["frac"], 4), "achieved": round(r["achieved"], 1),
+                                 "unit": r["unit"], "bound": r["bound"]}
+                             for k, r in rooflines.items()},
     }
+    if not args.no_train:
+        print("bench: train step", file=sys.stderr, flush=True)
+        line["train_step"] = train_step_line(B, max(5, args.steps // 5), 3)
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(p, min(args.cpu_sample, p.tokens))
+        line["cpu_baseline"] = cpu_baseline(p, inputs, min(args.cpu_sample, p.tokens))
     print(json.dumps(line), flush=True)
 
 
