@@ -25,7 +25,8 @@ int check(const moe_problem* p) {
       p->d_model < 1 || p->d_hidden < 1 || p->d_shared < 0)
     return MOE_ERR_INVALID;
   if (p->dtype != MOE_FP32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID;
-  if (p->block_m != 32 && p->block_m != 64 && p->block_m != 128) return MOE_ERR_UNSUPPORTED;
+  if (p->block_m != 32 && p->block_m != 64 && p->block_m != 128 && p->block_m != 256)
+    return MOE_ERR_UNSUPPORTED;
   if (p->experts > 64) return MOE_ERR_UNSUPPORTED;
   if (p->d_model % 128 != 0 || p->d_model > 8192) return MOE_ERR_UNSUPPORTED;
   if (p->d_hidden % 64 != 0 || p->d_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;

@@ -12,7 +12,7 @@
 //
 // Every reduction runs in a fixed order with one writer per output (no
 // floating-point atomics), so the gradients are deterministic.
-#include "gemm_core.h"
+#include "gemm_launch.h"
 
 namespace moe {
 
@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kRowThreads) void router_partial_kernel(
     const T* __restrict__ x, int d, int topk, const int32_t* __restrict__ perm,
     const float* __restrict__ dl, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, float* __restrict__ partial) {
-  __shared__ int64_t tok[128];
-  __shared__ float dv[128];
+  __shared__ int64_t tok[256];  // rows of one tile (block_m <= 256)
+  __shared__ float dv[256];
   const int tile = blockIdx.x;
   if (tile >= *num_tiles) return;
   const int row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
@@ -241,40 +241,6 @@ void zero(float* p, int64_t n, hipStream_t s) {
              0, s, p, n);
 }
 
-template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
-void gemm(const char* name, const GemmArgs& a, int64_t row_tiles, hipStream_t s) {
-  if (kDense) row_tiles = (a.M + Cfg::BM - 1) / Cfg::BM;
-  if (row_tiles <= 0) return;
-  const int64_t work = row_tiles * (a.N / Cfg::BN);
-  const int slots = persistent_slots(
-      reinterpret_cast<const void*>(&gemm_kernel<T, Cfg, kGather, kEpi, kDense>), Cfg::NT);
-  const unsigned grid = static_cast<unsigned>(work < slots ? work : slots);
-  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), dim3(grid), dim3(Cfg::NT), 0, s,
-             a, static_cast<int>(work));
-}
-
-// Grouped GEMM over the block_m tile list: the eight-wave 256-column tile
-// when N allows it, else the four-wave 128-column tile.
-template <typename T, bool kGather, int kEpi>
-void grouped_gemm(const char* name, const GemmArgs& a, int bm, int64_t max_tiles, hipStream_t s) {
-  const bool wide = a.N % 256 == 0;
-  if (bm == 128) {
-    if (wide) gemm<T, Cfg128W, kGather, kEpi, false>(name, a, max_tiles, s);
-    else gemm<T, Cfg128, kGather, kEpi, false>(name, a, max_tiles, s);
-  } else if (bm == 64) {
-    if (wide) gemm<T, Cfg64W, kGather, kEpi, false>(name, a, max_tiles, s);
-    else gemm<T, Cfg64, kGather, kEpi, false>(name, a, max_tiles, s);
-  } else {
-    gemm<T, Cfg32, kGather, kEpi, false>(name, a, max_tiles, s);
-  }
-}
-
-// Dense GEMM over all rows (shared expert).
-template <typename T, int kEpi>
-void dense_gemm(const char* name, const GemmArgs& a, hipStream_t s) {
-  if (a.N % 256 == 0) gemm<T, Cfg128W, false, kEpi, true>(name, a, 1, s);
-  else gemm<T, Cfg128, false, kEpi, true>(name, a, 1, s);
-}
 
 
 template <typename T, bool kGatherA, bool kDense>

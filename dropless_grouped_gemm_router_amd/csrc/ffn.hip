@@ -11,7 +11,7 @@
 // loads; gate and up are interleaved in 16-column groups so that one
 // 32-column MFMA tile carries matching gate and up columns and the SwiGLU
 // epilogue needs no data exchange.
-#include "gemm_core.h"
+#include "gemm_launch.h"
 
 namespace moe {
 
@@ -61,40 +61,6 @@ void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc
                      static_cast<T*>(dst), K, nsrc, il ? 1 : 0);
 }
 
-template <typename T, typename Cfg, bool kGather, int kEpi, bool kDense>
-void gemm(const char* name, const GemmArgs& a, int64_t row_tiles, hipStream_t s) {
-  if (kDense) row_tiles = (a.M + Cfg::BM - 1) / Cfg::BM;
-  if (row_tiles <= 0) return;
-  const int64_t work = row_tiles * (a.N / Cfg::BN);
-  const int slots = persistent_slots(
-      reinterpret_cast<const void*>(&gemm_kernel<T, Cfg, kGather, kEpi, kDense>), Cfg::NT);
-  const unsigned grid = static_cast<unsigned>(work < slots ? work : slots);
-  MOE_LAUNCH(name, (gemm_kernel<T, Cfg, kGather, kEpi, kDense>), dim3(grid), dim3(Cfg::NT), 0, s,
-             a, static_cast<int>(work));
-}
-
-// Grouped GEMM over the block_m tile list: the eight-wave 256-column tile
-// when N allows it, else the four-wave 128-column tile.
-template <typename T, bool kGather, int kEpi>
-void grouped_gemm(const char* name, const GemmArgs& a, int bm, int64_t max_tiles, hipStream_t s) {
-  const bool wide = a.N % 256 == 0;
-  if (bm == 128) {
-    if (wide) gemm<T, Cfg128W, kGather, kEpi, false>(name, a, max_tiles, s);
-    else gemm<T, Cfg128, kGather, kEpi, false>(name, a, max_tiles, s);
-  } else if (bm == 64) {
-    if (wide) gemm<T, Cfg64W, kGather, kEpi, false>(name, a, max_tiles, s);
-    else gemm<T, Cfg64, kGather, kEpi, false>(name, a, max_tiles, s);
-  } else {
-    gemm<T, Cfg32, kGather, kEpi, false>(name, a, max_tiles, s);
-  }
-}
-
-// Dense GEMM over all rows (shared expert).
-template <typename T, int kEpi>
-void dense_gemm(const char* name, const GemmArgs& a, hipStream_t s) {
-  if (a.N % 256 == 0) gemm<T, Cfg128W, false, kEpi, true>(name, a, 1, s);
-  else gemm<T, Cfg128, false, kEpi, true>(name, a, 1, s);
-}
 
 
 template <typename T>

@@ -54,10 +54,11 @@ struct GemmArgs {
   int hsplit;               // SwiGLU backward: column offset of the up gradient in c
 };
 
-template <int BM_, int WAVES_M_, int WAVES_N_, int WM_SUB_, int WN_SUB_, int WPE_ = 2>
+template <int BM_, int WAVES_M_, int WAVES_N_, int WM_SUB_, int WN_SUB_, int PF_ = 2>
 struct TileCfg {
   static constexpr int BM = BM_, WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int WPE = WPE_;  // waves per SIMD the register budget is sized for
+  static constexpr int WPE = 2;  // waves per SIMD the register budget is sized for
+  static constexpr int PF = PF_;  // K stages prefetched into registers (1 or 2)
   static constexpr int WM_SUB = WM_SUB_, WN_SUB = WN_SUB_;
   static constexpr int BN = WAVES_N * WN_SUB * 32;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;  // threads per workgroup
@@ -72,6 +73,11 @@ using Cfg32 = TileCfg<32, 1, 4, 1, 1>;
 // N (a whole gate|up block of width <= 128, or 256 model columns) per tile.
 using Cfg128W = TileCfg<128, 2, 4, 2, 2>;  // 128 x 256, waves 64 x 64
 using Cfg64W = TileCfg<64, 2, 4, 1, 2>;    // 64 x 256, waves 32 x 64
+// 256 x 256, waves 128 x 64, one stage of register prefetch (registers):
+// 128 MFMA flops per staged byte, twice the 128 x 128 tile.
+using Cfg256W = TileCfg<256, 2, 4, 4, 2, 1>;
+// 256 x 128 for N not a multiple of 256 (four waves, 64 x 128 each).
+using Cfg256N = TileCfg<256, 4, 1, 2, 4, 1>;
 
 constexpr int kStageBytes = 128;   // K bytes per row per stage
 constexpr int kLdsRowBytes = 144;  // + 16 bytes padding
@@ -324,13 +330,6 @@ void gemm_kernel(const GemmArgs p, int total_work) {
                                : nullptr;
     auto stage_b = [&](int st) { return st < ks_split ? b_base : b2_base; };
 
-    StageRegs<A_CH, B_CH> r0 = gemm_gload<A_CH, B_CH, NT>(a_src, b_base, b_row_bytes, 0);
-    StageRegs<A_CH, B_CH> r1 = r0;
-    if (nk > 1) r1 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(1), b_row_bytes, kStageBytes);
-    // Metadata of the next item (its row indices are fetched after this tile).
-    const int w1 = w + gx;
-    const TileInfo nxt = (w1 < w_end) ? tile_info<Cfg, kDense>(p, w1, n_tiles_n) : TileInfo{0, 0, 0};
-
     f32x16_t acc[WM_SUB][WN_SUB];
 #pragma unroll
     for (int i = 0; i < WM_SUB; ++i)
@@ -339,50 +338,41 @@ void gemm_kernel(const GemmArgs p, int total_work) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-    gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem, r0, lds_off);
+    // Metadata of the next item (its row indices are fetched after this tile).
+    const int w1 = w + gx;
+    const TileInfo nxt = (w1 < w_end) ? tile_info<Cfg, kDense>(p, w1, n_tiles_n) : TileInfo{0, 0, 0};
+    // Software pipeline with a ring of PF register stages: while stage s is
+    // multiplied out of LDS buffer s&1, stages s+1 .. s+PF-1 wait in
+    // registers and stage s+PF is in flight from memory, so PF stages of
+    // loads cover one memory latency. The scheduling fences keep loads
+    // before the MFMAs and the LDS store (which waits for its loads) after
+    // them; left alone, the compiler hoists the store and sinks the loads to
+    // save registers. The loop is unrolled by PF so ring slots are static.
+    constexpr int PF = Cfg::PF;
+    StageRegs<A_CH, B_CH> ring[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j)
+      if (j < nk) ring[j] = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(j), b_row_bytes, j * kStageBytes);
+    gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem, ring[0], lds_off);
     __syncthreads();
-    // Steady state (no branches): LDS buffer s&1 holds stage s, one register
-    // set holds stage s+1 and the other receives stage s+2. The scheduling
-    // fences keep that order: loads issue before the MFMAs and the LDS
-    // store (which waits for its loads) comes after them; left alone, the
-    // compiler hoists the store and sinks the loads to save registers,
-    // which shortens the prefetch distance to under one stage.
-    int s = 0;
-    for (; s + 3 < nk; s += 2) {
-      r0 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + 2), b_row_bytes, (s + 2) * kStageBytes);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, r1, lds_off);
-      __syncthreads();
-      r1 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + 3), b_row_bytes, (s + 3) * kStageBytes);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + ((s + 1) & 1) * bufb, a_frag, b_frag, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + (s & 1) * bufb, r0, lds_off);
-      __syncthreads();
-    }
-    // Tail: one to three stages remain (s in LDS, s+1 in r1).
-    if (s + 2 < nk) {
-      r0 = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + 2), b_row_bytes, (s + 2) * kStageBytes);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, r1, lds_off);
-      __syncthreads();
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + ((s + 1) & 1) * bufb, a_frag, b_frag, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + (s & 1) * bufb, r0, lds_off);
-      __syncthreads();
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
-    } else if (s + 1 < nk) {
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
-      __builtin_amdgcn_sched_barrier(0);
-      gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, r1, lds_off);
-      __syncthreads();
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + ((s + 1) & 1) * bufb, a_frag, b_frag, acc);
-    } else {
-      gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+    for (int s0 = 0; s0 < nk; s0 += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int s = s0 + j;
+        if (s < nk) {
+          if (s + PF < nk)
+            ring[j] = gemm_gload<A_CH, B_CH, NT>(a_src, stage_b(s + PF), b_row_bytes,
+                                                 (s + PF) * kStageBytes);
+          __builtin_amdgcn_sched_barrier(0);
+          gemm_compute<T, WM_SUB, WN_SUB>(smem + (s & 1) * bufb, a_frag, b_frag, acc);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s + 1 < nk) {
+            gemm_lstore<A_CH, B_CH, A_BYTES, NT>(smem + ((s + 1) & 1) * bufb, ring[(j + 1) % PF],
+                                                 lds_off);
+            __syncthreads();
+          }
+        }
+      }
     }
     // Row indices of the next item, while this tile's results drain.
     tile_rows<A_CH, NT, kGather>(p, nxt, tid, src_cur);

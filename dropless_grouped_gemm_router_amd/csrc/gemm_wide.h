@@ -1,0 +1,363 @@
+// Wide-tile grouped GEMM for bf16 on gfx950: 256 x 256 output tiles.
+//
+//   C[rows of a tile, n] = sum_k A[row, k] * B[group][n, k]
+//
+// Same operands, work list, epilogues and argument block as gemm_kernel
+// (gemm_core.h); this variant is the one sized for the chip:
+//
+//  * 512 threads = 8 waves as 4 (rows) x 2 (columns); each wave owns a
+//    64 x 128 block of 2 x 4 MFMA 32x32x16 tiles, i.e. 42.7 flops per byte
+//    of fragment read from LDS (a 64 x 64 wave block gives 32, which is at
+//    the LDS read rate of a CU at full MFMA issue).
+//  * The workgroup tile reads 128 flops per byte from L2, twice a 128 x 128
+//    tile, which is what keeps the L2-to-CU path off the critical path.
+//  * K stages of 64 elements (128 bytes per row) go from global memory
+//    straight into LDS with global_load_lds_dwordx4: no staging registers
+//    and no LDS store instructions. Two 64 KiB stage buffers, so a stage is
+//    in flight while the previous one is multiplied out; the first stage of
+//    the next work item is issued while the current item's last stage is
+//    multiplied out, so its load overlaps that stage and the epilogue.
+//  * A direct-to-LDS load writes 64 consecutive 16-byte pieces, so rows
+//    cannot be padded; instead the 16-byte chunk c of LDS row r sits at
+//    position c ^ ((r >> 1) & 7) of the row, which spreads the 32 rows one
+//    fragment read touches over all banks.
+#pragma once
+
+#include "gemm_core.h"
+
+namespace moe {
+
+struct WideCfg {
+  static constexpr int BM = 256, BN = 256;
+  static constexpr int WAVES_M = 4, WAVES_N = 2;
+  static constexpr int WM_SUB = 2, WN_SUB = 4;  // 32 x 32 MFMA tiles per wave
+  static constexpr int NT = 512;
+};
+
+constexpr int kWideRowBytes = 128;                   // K bytes per row per stage
+constexpr int kWideStage = 512 * kWideRowBytes;      // A rows 0..255, B rows 256..511
+constexpr int kWideLoads = 4;                        // A (and B) loads per lane per stage
+
+// Byte offset of 16-byte chunk c of LDS row r within a stage buffer.
+__device__ __forceinline__ int wide_swizzle(int r, int c) {
+  return r * kWideRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// Wait for this wave's outstanding vector-memory operations (the
+// direct-to-LDS loads count there) and LDS reads.
+__device__ __forceinline__ void wide_wait_all() {
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0x0 << 8));
+}
+
+// Every wave's loads for a stage have landed once each wave has waited for
+// its own and passed this barrier. The asm form carries no memory fence (a
+// fence would make the compiler wait for every outstanding load, including
+// the next stage's) and its clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void wide_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Issue one K stage into an LDS buffer. Load i of lane l in wave w covers
+// tile row r = (4 w + i) * 8 + l / 8, 16-byte position l % 8 of LDS row r
+// (and of row 256 + r for B); the lane's global addresses already point at
+// the chunk that belongs at that position.
+__device__ __forceinline__ void wide_issue(char* buf, const char* const (&a_row)[kWideLoads],
+                                           const char* b_base, const int (&b_off)[2],
+                                           int64_t b_step, int koff, int wave) {
+#pragma unroll
+  for (int i = 0; i < kWideLoads; ++i)
+    __builtin_amdgcn_global_load_lds(a_row[i] + koff, buf + (wave * kWideLoads + i) * 1024, 16, 0,
+                                     0);
+#pragma unroll
+  for (int i = 0; i < kWideLoads; ++i)
+    __builtin_amdgcn_global_load_lds(b_base + koff + b_off[i & 1] + i * b_step,
+                                     buf + 256 * kWideRowBytes + (wave * kWideLoads + i) * 1024,
+                                     16, 0, 0);
+}
+
+// Multiply one stage out of LDS: four 16-element K steps.
+__device__ __forceinline__ void wide_compute(const char* buf, int a_frag, int b_frag,
+                                             const int (&sw)[4],
+                                             f32x16_t (&acc)[WideCfg::WM_SUB][WideCfg::WN_SUB]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    u32x4 xf[WideCfg::WM_SUB], wf[WideCfg::WN_SUB];
+#pragma unroll
+    for (int i = 0; i < WideCfg::WM_SUB; ++i)
+      xf[i] = *reinterpret_cast<const u32x4*>(buf + a_frag + i * 32 * kWideRowBytes + sw[q]);
+#pragma unroll
+    for (int j = 0; j < WideCfg::WN_SUB; ++j)
+      wf[j] = *reinterpret_cast<const u32x4*>(buf + b_frag + j * 32 * kWideRowBytes + sw[q]);
+#pragma unroll
+    for (int i = 0; i < WideCfg::WM_SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < WideCfg::WN_SUB; ++j) Mfma<bf16_t>::step(wf[j], xf[i], acc[i][j]);
+  }
+}
+
+// Row indices behind the A loads of this lane for a work item, as read
+// (rows past the tile's end repeat its last row; their results are never
+// stored). In gather mode this is the flat slot; the token is slot / top_k,
+// taken only when the addresses are formed, so that the load's wait lands
+// where the stage loads are waited for anyway.
+template <bool kGather>
+__device__ __forceinline__ void wide_src_rows(const GemmArgs& p, const TileInfo& t, int lrow,
+                                              int (&src)[kWideLoads]) {
+#pragma unroll
+  for (int i = 0; i < kWideLoads; ++i) {
+    // An empty item (t.rows == 0, t.row0 == 0) reads slot 0, which exists
+    // whenever the kernel runs; the load is unconditional so that no branch
+    // writes its destination register while an older load may target it.
+    const int mr = max(0, min(lrow + 8 * i, t.rows - 1));
+    src[i] = kGather ? p.perm[t.row0 + mr] : t.row0 + mr;
+  }
+}
+
+template <bool kGather>
+__device__ __forceinline__ void wide_a_rows(const GemmArgs& p, const int (&src)[kWideLoads],
+                                            const int (&chunk_off)[2],
+                                            const char* (&a_row)[kWideLoads]) {
+  const int64_t a_row_bytes = p.lda * 2;
+#pragma unroll
+  for (int i = 0; i < kWideLoads; ++i) {
+    const int r = kGather ? src[i] / p.topk : src[i];
+    a_row[i] = static_cast<const char*>(p.a) + r * a_row_bytes + chunk_off[i & 1];
+  }
+}
+
+// Weight base of a work item (and of its second part, offset so that stage
+// s of either reads at s * 128 bytes).
+__device__ __forceinline__ void wide_b_bases(const GemmArgs& p, const TileInfo& t, int nt,
+                                             int64_t ldb, const char*& b1, const char*& b2) {
+  b1 = static_cast<const char*>(p.b) +
+       (static_cast<int64_t>(t.group) * p.b_group_stride + static_cast<int64_t>(nt) * 256 * ldb) * 2;
+  b2 = p.b2 ? static_cast<const char*>(p.b2) +
+                  (static_cast<int64_t>(t.group) * p.b2_group_stride +
+                   static_cast<int64_t>(nt) * 256 * ldb - p.ksplit) * 2
+            : b1;
+}
+
+// Epilogue through LDS. Stored straight from the accumulators, each store
+// instruction would touch 32 rows with 8 bytes each; instead each wave
+// writes its results as a 64-row x 128-byte block into a private 8 KiB LDS
+// region and stores it back as whole 128-byte row pieces (64 lanes x 16
+// bytes = 8 rows per instruction). Chunk c of region row r sits at position
+// c ^ (r & 7), so the accumulator-layout writes spread over the banks.
+__device__ __forceinline__ void wide_park(char* region, int row, int byte, float v0, float v1,
+                                          float v2, float v3) {
+  const int pos = (((byte >> 4) ^ (row & 7)) << 4) | (byte & 15);
+  uint2 u;
+  u.x = pack_bf16x2(v0, v1);
+  u.y = pack_bf16x2(v2, v3);
+  *reinterpret_cast<uint2*>(region + row * 128 + pos) = u;
+}
+
+// Writes the parked block: region row r goes to dst + r * ld (elements),
+// 64 bf16 columns, for rows r < rows.
+__device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int64_t ld, int rows,
+                                           int lane) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = k * 8 + (lane >> 3), c = lane & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+    if (r < rows) *reinterpret_cast<u32x4*>(dst + r * ld + c * 8) = v;
+  }
+}
+
+// Parks the wave's 64 x 64 block of SwiGLU results (kWhich 0), gate
+// pre-activations (1) or up pre-activations (2). Packed columns j*32 +
+// [0,16) are gate columns and j*32 + [16,32) the matching up columns, so
+// registers 4rr + q (rr < 2) hold gate and 4(rr + 2) + q the up values of
+// hidden column j*16 + 8rr + 4g + q of the block.
+template <int kWhich>
+__device__ __forceinline__ void wide_park_swiglu(
+    const f32x16_t (&acc)[WideCfg::WM_SUB][WideCfg::WN_SUB], char* region, int g, int r32) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a = acc[i][j][4 * rr + q], b = acc[i][j][4 * (rr + 2) + q];
+          v[q] = kWhich == 0 ? silu_f(a) * b : (kWhich == 1 ? a : b);
+        }
+        wide_park(region, i * 32 + r32, j * 32 + rr * 16 + g * 8, v[0], v[1], v[2], v[3]);
+      }
+}
+
+// Wave epilogue of one wide tile for the plain store and the forward SwiGLU.
+// Accumulator register q of MFMA tile (i, j) holds row i*32 + r32 and
+// column j*32 + 8*(q/4) + 4*g + q%4 of the wave's 64 x 128 block.
+template <int kEpi>
+__device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
+                                              const f32x16_t (&acc)[WideCfg::WM_SUB][WideCfg::WN_SUB],
+                                              char* region, int row0, int rows, int nt, int wm,
+                                              int wn, int g, int r32, int lane) {
+  const int wrows = rows - wm * 64;  // rows of this wave's block that exist
+  const int64_t orow = static_cast<int64_t>(row0) + wm * 64;
+  bf16_t* c = static_cast<bf16_t*>(p.c);
+  if (kEpi == kEpiStore) {
+    // Two passes of 64 columns (MFMA tiles j = 2h, 2h + 1).
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x16_t& a = acc[i][2 * h + jj];
+            wide_park(region, i * 32 + r32, jj * 64 + rr * 16 + g * 8, a[4 * rr], a[4 * rr + 1],
+                      a[4 * rr + 2], a[4 * rr + 3]);
+          }
+      const int col = nt * WideCfg::BN + wn * 128 + h * 64;
+      wide_drain(region, c + orow * p.ldc + col, p.ldc, wrows, lane);
+    }
+  } else {
+    const int hcol = nt * (WideCfg::BN / 2) + wn * 64;
+    wide_park_swiglu<0>(acc, region, g, r32);
+    wide_drain(region, c + orow * p.ldc + hcol, p.ldc, wrows, lane);
+    if (p.sa) {
+      wide_park_swiglu<1>(acc, region, g, r32);
+      wide_drain(region, static_cast<bf16_t*>(p.sa) + orow * p.lds + hcol, p.lds, wrows, lane);
+      wide_park_swiglu<2>(acc, region, g, r32);
+      wide_drain(region, static_cast<bf16_t*>(p.sb) + orow * p.lds + hcol, p.lds, wrows, lane);
+    }
+  }
+}
+
+// Row tile of work item w. The tile list arrives as separate restrict
+// arguments: nothing the kernel stores can alias it, so its reads compile to
+// scalar loads, whose waits do not hold up the in-flight stage loads.
+template <bool kDense>
+__device__ __forceinline__ TileInfo wide_tile(const GemmArgs& p, const int32_t* __restrict__ tiles,
+                                              const int32_t* __restrict__ num_tiles, int w,
+                                              int n_tiles_n) {
+  const int mt = w / n_tiles_n;
+  TileInfo t{0, 0, 0};
+  if (kDense) {
+    t.row0 = mt * WideCfg::BM;
+    const int64_t left = p.M - t.row0;
+    t.rows = left <= 0 ? 0 : static_cast<int>(left < WideCfg::BM ? left : WideCfg::BM);
+  } else if (mt < *num_tiles) {
+    t.group = tiles[3 * mt + 0];
+    t.row0 = tiles[3 * mt + 1];
+    t.rows = tiles[3 * mt + 2];
+  }
+  return t;
+}
+
+// Persistent wide-tile GEMM (bf16). Work assignment as in gemm_kernel: the
+// workgroups of XCD x walk its contiguous share of the (row tile, N tile)
+// list, so one expert's tiles, and its weights, stay in one L2. `tiles` and
+// `num_tiles` are p.tiles and p.num_tiles (unused in dense mode).
+template <bool kGather, int kEpi, bool kDense>
+__global__ __launch_bounds__(WideCfg::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
+                      const int32_t* __restrict__ num_tiles, int total_work) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kWideStage];
+  const int n_tiles_n = p.N / WideCfg::BN;
+  const int G = gridDim.x;
+  const int nx = G < 8 ? G : 8;
+  const int x = blockIdx.x % nx, wi = blockIdx.x / nx;
+  const int gx = G / nx + (x < G % nx ? 1 : 0);
+  const int per = (total_work + nx - 1) / nx;
+  const int w_end = min(total_work, (x + 1) * per);
+  int w = x * per + wi;
+  if (w >= w_end) return;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int wm = wave / WideCfg::WAVES_N, wn = wave % WideCfg::WAVES_N;
+  const int64_t ldb = p.ldb ? p.ldb : p.K;
+  const int64_t b_step = 16 * ldb;  // 8 rows
+  const int nk = p.K / 64;
+  const int ks_split = p.b2 ? p.ksplit / 64 : (1 << 30);
+
+  // Load side: lane's first row, and the chunk it fetches for even and odd
+  // loads ((row >> 1) & 7 of row lrow + 8 i is (lane >> 4) + 4 (i & 1)).
+  const int lrow = wave * kWideLoads * 8 + (lane >> 3);
+  const int xr = lane >> 4;
+  const int chunk_off[2] = {((lane & 7) ^ xr) * 16, ((lane & 7) ^ (xr + 4)) * 16};
+  const int b_off[2] = {static_cast<int>(lrow * ldb * 2) + chunk_off[0],
+                        static_cast<int>(lrow * ldb * 2) + chunk_off[1]};
+  // Fragment side: rows wm * 64 + r32 (A) and 256 + wn * 128 + r32 (B), and
+  // the swizzled position of K step q's chunk 2 q + g.
+  const int a_frag = (wm * WideCfg::WM_SUB * 32 + r32) * kWideRowBytes;
+  const int b_frag = (256 + wn * WideCfg::WN_SUB * 32 + r32) * kWideRowBytes;
+  int sw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sw[q] = ((2 * q + g) ^ ((r32 >> 1) & 7)) << 4;
+
+  TileInfo cur = wide_tile<kDense>(p, tiles, num_tiles, w, n_tiles_n);
+  if (cur.rows <= 0) return;
+  int src[kWideLoads];
+  wide_src_rows<kGather>(p, cur, lrow, src);
+  const char* a_cur[kWideLoads];
+  wide_a_rows<kGather>(p, src, chunk_off, a_cur);
+  const char *b1_cur, *b2_cur;
+  wide_b_bases(p, cur, w % n_tiles_n, ldb, b1_cur, b2_cur);
+
+  int buf = 0;
+  wide_issue(smem, a_cur, b1_cur, b_off, b_step, 0, wave);
+
+  while (true) {
+    const int nt = w % n_tiles_n;
+    const int w1 = w + gx;
+    TileInfo nxt{0, 0, 0};
+
+    f32x16_t acc[WideCfg::WM_SUB][WideCfg::WN_SUB];
+#pragma unroll
+    for (int i = 0; i < WideCfg::WM_SUB; ++i)
+#pragma unroll
+      for (int j = 0; j < WideCfg::WN_SUB; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    for (int s = 0; s < nk; ++s) {
+      wide_wait_all();
+      wide_barrier();
+      char* nb = smem + (buf ^ 1) * kWideStage;
+      // The next item's metadata and row indices are read during this
+      // item's first stage (before its issue only when there is one stage).
+      if (s == 0 && nk == 1) {
+        nxt = (w1 < w_end) ? wide_tile<kDense>(p, tiles, num_tiles, w1, n_tiles_n) : TileInfo{0, 0, 0};
+        wide_src_rows<kGather>(p, nxt, lrow, src);
+      }
+      if (s + 1 < nk) {
+        wide_issue(nb, a_cur, (s + 1) < ks_split ? b1_cur : b2_cur, b_off, b_step, (s + 1) * 128,
+                   wave);
+      } else if (nxt.rows > 0) {
+        wide_a_rows<kGather>(p, src, chunk_off, a_cur);
+        wide_b_bases(p, nxt, w1 % n_tiles_n, ldb, b1_cur, b2_cur);
+        wide_issue(nb, a_cur, b1_cur, b_off, b_step, 0, wave);
+      }
+      if (s == 0 && nk > 1) {
+        nxt = (w1 < w_end) ? wide_tile<kDense>(p, tiles, num_tiles, w1, n_tiles_n) : TileInfo{0, 0, 0};
+        wide_src_rows<kGather>(p, nxt, lrow, src);
+      }
+      wide_compute(smem + buf * kWideStage, a_frag, b_frag, sw, acc);
+      buf ^= 1;
+    }
+
+    if (kEpi != kEpiStore) {
+      // SwiGLU outputs are half the tile (or read saved values): stored
+      // straight from the accumulators.
+      gemm_epilogue<bf16_t, WideCfg, kEpi>(p, acc, cur.row0, cur.rows, nt, wm, wn, g, r32);
+    } else {
+      // The buffer of the last stage is free once every wave is done with it
+      // (the other one is receiving the next item's first stage).
+      wide_barrier();
+      wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192, cur.row0,
+                          cur.rows, nt, wm, wn, g, r32, lane);
+    }
+
+    if (nxt.rows <= 0) break;
+    w = w1;
+    cur = nxt;
+  }
+}
+
+}  // namespace moe

@@ -177,13 +177,14 @@ def make_inputs(p: Problem, seed: int = 0, with_grad_out: bool = False,
 
 # The workloads the layer is measured on (the pages' problem fields; shapes
 # as stated with each workload). Index 3 is the headline forward workload and
-# index 4 the train step.
+# index 4 the train step. bf16 forward workloads cut expert rows into
+# 256-row tiles, the row tile of the 256 x 256 MFMA engine.
 WORKLOADS = {
     0: ("fwd fp32, 4096 tok, E8 top-2, d512 h1024", Problem(4096, 8, 2, 512, 1024, 0, "fp32", 128), "fwd"),
-    1: ("fwd bf16, 32768 tok, E8 top-2, d512 h1024", Problem(32768, 8, 2, 512, 1024, 0, "bf16", 128), "fwd"),
-    2: ("fwd bf16, 32768 tok, E64 top-4, d512 h256", Problem(32768, 64, 4, 512, 256, 0, "bf16", 128), "fwd"),
+    1: ("fwd bf16, 32768 tok, E8 top-2, d512 h1024", Problem(32768, 8, 2, 512, 1024, 0, "bf16", 256), "fwd"),
+    2: ("fwd bf16, 32768 tok, E64 top-4, d512 h256", Problem(32768, 64, 4, 512, 256, 0, "bf16", 256), "fwd"),
     3: ("fwd bf16, 131072 tok, E64 top-8, d512 h128, shared 1024",
-        Problem(131072, 64, 8, 512, 128, 1024, "bf16", 128), "fwd"),
+        Problem(131072, 64, 8, 512, 128, 1024, "bf16", 256), "fwd"),
     4: ("train bf16, 16384 tok, E64 top-8, d512 h128, shared 1024",
         Problem(16384, 64, 8, 512, 128, 1024, "bf16", 128), "train"),
 }

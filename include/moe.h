@@ -65,7 +65,8 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
  * d_model, d_hidden, dtype (kernel_gmm_gpu.json "results" records), the
  * shared expert width (gpu_moe_h100.json records, field "shared") and the
  * grouped-GEMM row tile block_m (kernel_gmm_gpu.json config blocks,
- * "block_m" / "block_ms": 32, 64, 128).
+ * "block_m" / "block_ms": 32, 64, 128 on the pages' hardware; 256 is
+ * supported too and is the gfx950 choice for large problems).
  *
  * dtype is the storage type of x, the expert and shared weights, the
  * sorted expert outputs, the shared-expert output, out, grad_out, grad_x
@@ -78,7 +79,7 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
  * Supported (else MOE_ERR_UNSUPPORTED): 1 <= experts <= 64,
  * 1 <= top_k <= experts, d_model a multiple of 128 (at most 8192),
  * d_hidden and d_shared multiples of 64 (d_shared may be 0), block_m in
- * {32, 64, 128}, tokens*top_k < 2^31.
+ * {32, 64, 128, 256}, tokens*top_k < 2^31.
  */
 typedef struct {
   int64_t tokens;

@@ -50,6 +50,8 @@ def test_param_count_and_tiles():
     (dict(d_shared=-64), B.MOE_ERR_INVALID),
     (dict(experts=65, top_k=2), B.MOE_ERR_UNSUPPORTED),
     (dict(block_m=48), B.MOE_ERR_UNSUPPORTED),
+    (dict(block_m=512), B.MOE_ERR_UNSUPPORTED),
+    (dict(block_m=256), B.MOE_OK),
     (dict(d_model=500), B.MOE_ERR_UNSUPPORTED),
     (dict(d_hidden=100), B.MOE_ERR_UNSUPPORTED),
     (dict(d_shared=96), B.MOE_ERR_UNSUPPORTED),

@@ -47,6 +47,8 @@ SMALL = [
     Problem(3, 4, 2, 128, 128, 128, "bf16", 32),
     Problem(200, 5, 5, 128, 128, 0, "fp32", 64),
     Problem(1000, 64, 8, 128, 128, 256, "bf16", 128),
+    Problem(1500, 8, 2, 256, 128, 128, "bf16", 256),
+    Problem(700, 4, 2, 256, 256, 128, "fp32", 256),
 ]
 
 

@@ -37,6 +37,8 @@ SMALL = [
     Problem(97, 1, 1, 128, 64, 0, "bf16", 128),
     Problem(200, 5, 5, 128, 64, 0, "fp32", 64),
     Problem(1000, 64, 8, 128, 64, 64, "bf16", 128),
+    Problem(1500, 8, 2, 256, 128, 128, "bf16", 256),
+    Problem(700, 4, 2, 256, 256, 0, "fp32", 256),
 ]
 
 
