@@ -38,7 +38,7 @@ def test_param_count_and_tiles():
     assert B.moe_max_tiles(p) == 8192 // 64 + 8
     p3 = WORKLOADS[3][1]
     assert B.moe_param_count(p3) == 3 * 64 * 512 * 128 + 512 * 64 + 3 * 512 * 1024
-    assert B.moe_max_tiles(p3) == 131072 * 8 // 128 + 64
+    assert B.moe_max_tiles(p3) == 131072 * 8 // p3.block_m + 64
 
 
 @pytest.mark.parametrize("kw,code", [
