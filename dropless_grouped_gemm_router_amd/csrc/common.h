@@ -94,6 +94,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workgroups of `kernel` (block size `threads`) the current device keeps
 // resident at once: CUs x workgroups per CU (cached per device and kernel).
 int persistent_slots(const void* kernel, int threads);
+// Compute units of the current device.
+int cu_count();
 
 // Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).
 void trace_push(hipStream_t s, const char* name);

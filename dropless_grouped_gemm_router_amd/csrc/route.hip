@@ -2,15 +2,15 @@
 // weights, one fused kernel (kernel_gmm_gpu.json "pieces" suite, piece
 // "route").
 //
-// Lane layout: a token group of EP lanes (EP = next power of two >= E)
-// holds one token's logits, lane e of the group owning expert e; each lane
-// evaluates R tokens for its expert so every router value read from LDS
-// feeds R fused multiply-adds. Logits are the fixed fp32 chain
-// acc = fma(x[t,j], W[j,e], acc) for j ascending from +0.0, evaluated in
-// exactly that order (the chunking over j below only pauses the chain).
-// The selection runs k rounds of a butterfly argmax inside the group on
-// (logit descending, expert index ascending); no floating-point reduction
-// decides an expert.
+// Logits are the fixed fp32 chain acc = fma(x[t,j], W[j,e], acc) for j
+// ascending from +0.0, evaluated in exactly that order; the blocking below
+// only pauses the chain. A token group of L lanes holds one token's
+// logits, each lane P experts of R tokens, so every router value read from
+// LDS feeds R multiply-adds and every token value P. The selection runs k
+// rounds of a butterfly argmax inside the group on (logit descending,
+// expert index ascending); no floating-point reduction decides an expert.
+// Routers that fit in LDS stay resident for a CU's whole token range
+// (route_resident_kernel); larger ones are streamed in row chunks.
 #include "common.h"
 
 namespace moe {
@@ -35,11 +35,107 @@ __device__ __forceinline__ void load8(const float* p, float* o) {
   o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
 }
 
+// Eight values from their raw 16-byte pieces.
+template <typename T>
+__device__ __forceinline__ void widen8(const u32x4 (&v)[sizeof(T) / 2], float* o);
+template <>
+__device__ __forceinline__ void widen8<bf16_t>(const u32x4 (&v)[1], float* o) {
+  o[0] = bf16lo(v[0].x); o[1] = bf16hi(v[0].x);
+  o[2] = bf16lo(v[0].y); o[3] = bf16hi(v[0].y);
+  o[4] = bf16lo(v[0].z); o[5] = bf16hi(v[0].z);
+  o[6] = bf16lo(v[0].w); o[7] = bf16hi(v[0].w);
+}
+template <>
+__device__ __forceinline__ void widen8<float>(const u32x4 (&v)[2], float* o) {
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    o[4 * n + 0] = __uint_as_float(v[n].x);
+    o[4 * n + 1] = __uint_as_float(v[n].y);
+    o[4 * n + 2] = __uint_as_float(v[n].z);
+    o[4 * n + 3] = __uint_as_float(v[n].w);
+  }
+}
+
 // a ranks before b: valid before invalid, then larger logit, then lower index.
 __device__ __forceinline__ bool ranks_before(float av, int ae, float bv, int be) {
   const bool a_ok = ae < 0x10000, b_ok = be < 0x10000;
   if (a_ok != b_ok) return a_ok;
   return (av > bv) || (av == bv && ae < be);
+}
+
+// Top-k per token from a lane's logits acc[q][r] (expert le + q L, token
+// t0 + r): k rounds of argmax, first over the lane's own P experts, then a
+// butterfly over the L lanes of the group; then the renormalised weights.
+template <int L, int P, int R>
+__device__ __forceinline__ void route_select(const float (&acc)[P][R], int le, int64_t t0,
+                                             int64_t ntok, int E, int k,
+                                             int32_t* __restrict__ topk_idx,
+                                             float* __restrict__ topk_w) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t t = t0 + r;
+    bool taken[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) taken[q] = (le + q * L) >= E;
+    // Rank i (< k <= L * P) is kept by lane i % L of the group, in slot i / L.
+    float my_v[P], vmax = 0.0f;
+    int my_e[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      my_v[q] = 0.0f;
+      my_e[q] = 0;
+    }
+    for (int i = 0; i < k; ++i) {
+      float bv = acc[0][r];
+      int be = taken[0] ? (0x10000 + le) : le;
+#pragma unroll
+      for (int q = 1; q < P; ++q) {
+        const int eq = le + q * L;
+        const int ce = taken[q] ? (0x10000 + eq) : eq;
+        if (ranks_before(acc[q][r], ce, bv, be)) {
+          bv = acc[q][r];
+          be = ce;
+        }
+      }
+#pragma unroll
+      for (int off = L / 2; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, L);
+        const int oe = __shfl_xor(be, off, L);
+        if (ranks_before(ov, oe, bv, be)) {
+          bv = ov;
+          be = oe;
+        }
+      }
+      if (i == 0) vmax = bv;
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        if (be == le + q * L) taken[q] = true;
+        if (i == q * L + le) {
+          my_v[q] = bv;
+          my_e[q] = be;
+        }
+      }
+    }
+    // Weights exp(l_i - l_0) / sum over the k kept ranks.
+    float u[P], sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      u[q] = (q * L + le < k) ? expf(my_v[q] - vmax) : 0.0f;
+      sum += u[q];
+    }
+#pragma unroll
+    for (int off = L / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, L);
+    if (t < ntok) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int i = q * L + le;
+        if (i < k) {
+          topk_idx[t * k + i] = my_e[q];
+          topk_w[t * k + i] = u[q] / sum;
+        }
+      }
+    }
+  }
 }
 
 // Lane layout: a token group of L lanes covers one token's experts, lane
@@ -107,78 +203,120 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const T* __restric
     }
   }
 
-  // Top-k per token: k rounds of argmax, first over the lane's own P
-  // experts, then a butterfly over the L lanes of the group.
+  route_select<L, P, R>(acc, le, tok0 + grp * R, ntok, E, k, topk_idx, topk_w);
+}
+
+// Resident-router variant: one 1024-thread workgroup per CU keeps the whole
+// router (all d rows, transposed to [e][j]) in LDS for its lifetime and
+// walks token passes of (1024 / L) * R tokens, so W is read from memory
+// once per CU. Same lane layout and the same fp32 chain per logit as
+// route_kernel; the next 8 token values of each row are loaded while the
+// current 8 are multiplied in.
+constexpr int kResidentThreads = 1024;
+
+template <typename T, int L, int P, int R>
+__global__ __launch_bounds__(kResidentThreads) void route_resident_kernel(
+    const T* __restrict__ x, const float* __restrict__ wr, int64_t ntok, int d, int E, int k,
+    int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int EPAD = L * P;
+  constexpr int XN = static_cast<int>(sizeof(T)) / 2;  // 16-byte pieces per 8 values
+  constexpr int kPerPiece = 16 / static_cast<int>(sizeof(T));
+  extern __shared__ __attribute__((aligned(16))) float w_res[];  // [EPAD][d + kRoutePad]
+  const int stride = d + kRoutePad;
+  for (int i = threadIdx.x; i < d * EPAD; i += kResidentThreads) {
+    const int jj = i / EPAD, ee = i % EPAD;
+    w_res[ee * stride + jj] = (ee < E) ? wr[static_cast<int64_t>(jj) * E + ee] : 0.0f;
+  }
+  __syncthreads();
+
+  constexpr int kTokPerPass = (kResidentThreads / 64) * (64 / L) * R;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int le = lane % L, grp = lane / L;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * kTokPerPass; base < ntok;
+       base += static_cast<int64_t>(gridDim.x) * kTokPerPass) {
+    const int64_t t0 = base + (wave * (64 / L) + grp) * R;
+    const T* xrow[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t t = tok0 + grp * R + r;
-    bool taken[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) taken[q] = (le + q * L) >= E;
-    // Rank i (< k <= L * P) is kept by lane i % L of the group, in slot i / L.
-    float my_v[P], vmax = 0.0f;
-    int my_e[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      my_v[q] = 0.0f;
-      my_e[q] = 0;
+    for (int r = 0; r < R; ++r) {
+      int64_t t = t0 + r;
+      if (t >= ntok) t = ntok - 1;  // clamped for the tail; not stored
+      xrow[r] = x + t * d;
     }
-    for (int i = 0; i < k; ++i) {
-      float bv = acc[0][r];
-      int be = taken[0] ? (0x10000 + le) : le;
+    float acc[P][R];
 #pragma unroll
-      for (int q = 1; q < P; ++q) {
-        const int eq = le + q * L;
-        const int ce = taken[q] ? (0x10000 + eq) : eq;
-        if (ranks_before(acc[q][r], ce, bv, be)) {
-          bv = acc[q][r];
-          be = ce;
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[q][r] = 0.0f;
+    u32x4 xn[R][XN];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int n = 0; n < XN; ++n) xn[r][n] = *reinterpret_cast<const u32x4*>(xrow[r] + n * kPerPiece);
+
+    for (int jj = 0; jj < d; jj += 8) {
+      u32x4 xc[R][XN];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int n = 0; n < XN; ++n) xc[r][n] = xn[r][n];
+      if (jj + 8 < d) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int n = 0; n < XN; ++n)
+            xn[r][n] = *reinterpret_cast<const u32x4*>(xrow[r] + jj + 8 + n * kPerPiece);
+      }
+      // Router values four j at a time; each logit still takes j ascending.
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float wv[P][4];
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+          const float4 w4 =
+              *reinterpret_cast<const float4*>(w_res + (le + q * L) * stride + jj + 4 * h);
+          wv[q][0] = w4.x; wv[q][1] = w4.y; wv[q][2] = w4.z; wv[q][3] = w4.w;
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float xv[8];
+          widen8<T>(xc[r], xv);
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq)
+#pragma unroll
+            for (int q = 0; q < P; ++q)
+              acc[q][r] = __builtin_fmaf(xv[4 * h + jq], wv[q][jq], acc[q][r]);
         }
       }
-#pragma unroll
-      for (int off = L / 2; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, L);
-        const int oe = __shfl_xor(be, off, L);
-        if (ranks_before(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if (i == 0) vmax = bv;
-#pragma unroll
-      for (int q = 0; q < P; ++q) {
-        if (be == le + q * L) taken[q] = true;
-        if (i == q * L + le) {
-          my_v[q] = bv;
-          my_e[q] = be;
-        }
-      }
     }
-    // Weights exp(l_i - l_0) / sum over the k kept ranks.
-    float u[P], sum = 0.0f;
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      u[q] = (q * L + le < k) ? expf(my_v[q] - vmax) : 0.0f;
-      sum += u[q];
-    }
-#pragma unroll
-    for (int off = L / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, L);
-    if (t < ntok) {
-#pragma unroll
-      for (int q = 0; q < P; ++q) {
-        const int i = q * L + le;
-        if (i < k) {
-          topk_idx[t * k + i] = my_e[q];
-          topk_w[t * k + i] = u[q] / sum;
-        }
-      }
-    }
+    route_select<L, P, R>(acc, le, t0, ntok, E, k, topk_idx, topk_w);
   }
 }
 
 template <typename T, int L, int P, int R>
-hipError_t launch_route_t(const void* x, const float* wr, int64_t T_, int d, int E, int k,
-                          int32_t* idx, float* w, hipStream_t s) {
+size_t resident_lds_bytes(int d) {
+  return static_cast<size_t>(L) * P * (d + kRoutePad) * sizeof(float);
+}
+
+template <typename T, int L, int P, int R>
+hipError_t launch_route_resident(const void* x, const float* wr, int64_t T_, int d, int E, int k,
+                                 int32_t* idx, float* w, hipStream_t s) {
+  const size_t lds = resident_lds_bytes<T, L, P, R>(d);
+  auto kern = route_resident_kernel<T, L, P, R>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(lds));
+  if (e != hipSuccess) return e;
+  constexpr int kTokPerPass = (kResidentThreads / 64) * (64 / L) * R;
+  const int64_t passes = (T_ + kTokPerPass - 1) / kTokPerPass;
+  const int64_t blocks = passes < cu_count() ? passes : cu_count();
+  MOE_LAUNCH("route", kern, dim3(static_cast<unsigned>(blocks)), dim3(kResidentThreads), lds, s,
+             static_cast<const T*>(x), wr, T_, d, E, k, idx, w);
+  return hipGetLastError();
+}
+
+template <typename T, int L, int P, int R>
+hipError_t launch_route_chunked(const void* x, const float* wr, int64_t T_, int d, int E, int k,
+                                int32_t* idx, float* w, hipStream_t s) {
   constexpr int kTokPerBlock = (kRouteThreads / 64) * (64 / L) * R;
   const int64_t blocks = (T_ + kTokPerBlock - 1) / kTokPerBlock;
   MOE_LAUNCH("route", (route_kernel<T, L, P, R>), dim3(static_cast<unsigned>(blocks)),
@@ -186,16 +324,29 @@ hipError_t launch_route_t(const void* x, const float* wr, int64_t T_, int d, int
   return hipGetLastError();
 }
 
+// The router stays resident in LDS when it fits (E <= 64 at d <= 636, the
+// padded expert count times d + 4 floats within 160 KiB); larger routers
+// are streamed through LDS in 128-row chunks per 256-thread workgroup.
 template <typename T>
 hipError_t launch_route_dt(const void* x, const float* wr, int64_t T_, int d, int E, int k,
                            int32_t* idx, float* w, hipStream_t s) {
-  if (E <= 1) return launch_route_t<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 2) return launch_route_t<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 4) return launch_route_t<T, 4, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 8) return launch_route_t<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 16) return launch_route_t<T, 4, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
-  if (E <= 32) return launch_route_t<T, 8, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
-  return launch_route_t<T, 16, 4, 8>(x, wr, T_, d, E, k, idx, w, s);
+  const int epad = E <= 4 ? 4 : (E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)));
+  if (E <= 64 && static_cast<size_t>(epad) * (d + kRoutePad) * sizeof(float) <= 160 * 1024) {
+    if (E <= 1) return launch_route_resident<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+    if (E <= 2) return launch_route_resident<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+    if (E <= 4) return launch_route_resident<T, 4, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
+    if (E <= 8) return launch_route_resident<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
+    if (E <= 16) return launch_route_resident<T, 4, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
+    if (E <= 32) return launch_route_resident<T, 8, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
+    return launch_route_resident<T, 16, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
+  }
+  if (E <= 1) return launch_route_chunked<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 2) return launch_route_chunked<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 4) return launch_route_chunked<T, 4, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 8) return launch_route_chunked<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 16) return launch_route_chunked<T, 4, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
+  if (E <= 32) return launch_route_chunked<T, 8, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
+  return launch_route_chunked<T, 16, 4, 8>(x, wr, T_, d, E, k, idx, w, s);
 }
 
 }  // namespace
