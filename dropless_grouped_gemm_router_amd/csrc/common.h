@@ -38,8 +38,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-__device__ __forceinline__ float silu_f(float a) { return a / (1.0f + __expf(-a)); }
-__device__ __forceinline__ float sigmoid_f(float a) { return 1.0f / (1.0f + __expf(-a)); }
+// The hardware reciprocal (1 ulp) instead of an IEEE division: a few
+// instructions instead of a dozen per element. Large |a| behaves as the
+// division: exp(-a) = inf gives 0, exp(-a) = 0 gives 1.
+__device__ __forceinline__ float sigmoid_f(float a) { return __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
+__device__ __forceinline__ float silu_f(float a) { return a * sigmoid_f(a); }
 
 // Elements of one storage type per 16-byte chunk.
 template <typename T>
