@@ -143,11 +143,30 @@ __global__ __launch_bounds__(kRowThreads) void router_reduce_kernel(
 }
 
 // dx[t] = sum_i dX_sorted[slot(t,i)] + sum_i dl_i W_r[:, e_i] + dx_shared[t].
+// wrT[e][j] = wr[j][e]: the router columns as contiguous rows, so the
+// router term of dx reads 16- or 32-byte pieces instead of strided floats.
+__global__ __launch_bounds__(256) void router_transpose_kernel(const float* __restrict__ wr,
+                                                               int d, int E,
+                                                               float* __restrict__ wrT) {
+  __shared__ float tile[32][33];
+  const int j0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  for (int r = ty; r < 32; r += 8) {
+    const int j = j0 + r, e = e0 + tx;
+    tile[r][tx] = (j < d && e < E) ? wr[static_cast<int64_t>(j) * E + e] : 0.0f;
+  }
+  __syncthreads();
+  for (int r = ty; r < 32; r += 8) {
+    const int e = e0 + r, j = j0 + tx;
+    if (e < E && j < d) wrT[static_cast<int64_t>(e) * d + j] = tile[tx][r];
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
     int64_t ntok, int k, int d, int E, const T* __restrict__ dxs, const int32_t* __restrict__ inv_perm,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
-    const float* __restrict__ wr, const T* __restrict__ dx_shared, T* __restrict__ dx) {
+    const float* __restrict__ wrT, const T* __restrict__ dx_shared, T* __restrict__ dx) {
   constexpr int N = V16<T>::N;
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRowThreads / 64) + (threadIdx.x >> 6);
@@ -160,11 +179,15 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
       const int64_t slot = inv_perm[t * k + i];
       const int e = topk_idx[t * k + i];
       const float li = dl[t * k + i];
-      float v[N];
+      float v[N], wv[N];
       V16<T>::load(dxs + slot * d + c, v);
 #pragma unroll
-      for (int q = 0; q < N; ++q)
-        acc[q] += __builtin_fmaf(li, wr[static_cast<int64_t>(c + q) * E + e], v[q]);
+      for (int q = 0; q < N; q += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wrT + static_cast<int64_t>(e) * d + c + q);
+        wv[q] = w4.x; wv[q + 1] = w4.y; wv[q + 2] = w4.z; wv[q + 3] = w4.w;
+      }
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += __builtin_fmaf(li, wv[q], v[q]);
     }
     if (dx_shared) {
       float v[N];
@@ -200,7 +223,7 @@ __global__ __launch_bounds__(kRowThreads) void fill_zero_kernel(float* __restric
 }
 
 struct BwdLayout {
-  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, total;
+  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, total;
   int ks_sd, ks_sgu;
 };
 
@@ -229,6 +252,7 @@ BwdLayout bwd_layout(const moe_problem& p) {
   L.dxs = o;      o = align_up(o + T * d * es, 256);
   L.part_sd = o;  o = align_up(o + static_cast<size_t>(L.ks_sd) * hs * d * 4, 256);
   L.part_sgu = o; o = align_up(o + static_cast<size_t>(L.ks_sgu) * d * 2 * hs * 4, 256);
+  L.wrT = o;      o = align_up(o + static_cast<size_t>(p.experts) * d * 4, 256);
   L.total = o;
   return L;
 }
@@ -427,8 +451,11 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
                g.ws_up);
   }
   // dx: gather-sum of the routed input gradients plus the router and shared terms
+  float* wrT = reinterpret_cast<float*>(W + L.wrT);
+  MOE_LAUNCH("bwd_router_transpose", router_transpose_kernel, dim3((d + 31) / 32, (E + 31) / 32),
+             dim3(256), 0, s, w.w_router, d, E, wrT);
   MOE_LAUNCH("bwd_dx", dx_gather_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
-             dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, w.w_router,
+             dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, wrT,
              static_cast<const T*>(dxs), static_cast<T*>(grad_x));
   return hipGetLastError();
 }

@@ -332,13 +332,22 @@ hipError_t launch_route_dt(const void* x, const float* wr, int64_t T_, int d, in
                            int32_t* idx, float* w, hipStream_t s) {
   const int epad = E <= 4 ? 4 : (E <= 8 ? 8 : (E <= 16 ? 16 : (E <= 32 ? 32 : 64)));
   if (E <= 64 && static_cast<size_t>(epad) * (d + kRoutePad) * sizeof(float) <= 160 * 1024) {
+    // Tokens per lane R: the largest of 4, 2, 1 that still gives every CU a
+    // workgroup (fewer tokens per pass for small batches).
+    const int64_t cus = cu_count();
+    auto fits = [&](int L, int R) { return T_ >= cus * (kResidentThreads / L) * R; };
     if (E <= 1) return launch_route_resident<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 2) return launch_route_resident<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 4) return launch_route_resident<T, 4, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 8) return launch_route_resident<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 16) return launch_route_resident<T, 4, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
-    if (E <= 32) return launch_route_resident<T, 8, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
-    return launch_route_resident<T, 16, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
+    if (E <= 32) {
+      if (fits(8, 2)) return launch_route_resident<T, 8, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
+      return launch_route_resident<T, 8, 4, 1>(x, wr, T_, d, E, k, idx, w, s);
+    }
+    if (fits(16, 4)) return launch_route_resident<T, 16, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
+    if (fits(16, 2)) return launch_route_resident<T, 16, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
+    return launch_route_resident<T, 16, 4, 1>(x, wr, T_, d, E, k, idx, w, s);
   }
   if (E <= 1) return launch_route_chunked<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
   if (E <= 2) return launch_route_chunked<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
