@@ -28,7 +28,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_VALU_TFLOPS = 78.6
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["gemm_core.h", "ffn.hip", "route.hip", "permute.hip", "combine.hip", "common.h"]
+KERNEL_SOURCES = ["gemm_core.h", "gemm_wide.h", "gemm_launch.h", "ffn.hip", "route.hip",
+                  "permute.hip", "combine.hip", "common.h"]
 
 
 def kernel_source_hash():
@@ -40,45 +41,53 @@ def kernel_source_hash():
 
 
 def work(p):
-    """Algorithmic work of each forward kernel per launch: (kind, amount).
+    """Algorithmic work of each forward kernel per launch: (flops, bytes).
     FLOPs count a multiply-add as 2; bytes are the minimum each kernel must
-    move (inputs read once, outputs written once)."""
+    move through HBM (each input read once, each output written once)."""
     T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
     S = T * k
     es = 2 if p.dtype == "bf16" else 4
     w = {
-        "route": ("flop", 2 * T * d * E),
-        "gemm_gate_up": ("flop", 2 * S * d * 2 * h),
-        "gemm_down": ("flop", 2 * S * h * d),
+        # x and the router read, indices and weights written
+        "route": (2 * T * d * E, T * d * es + d * E * 4 + S * 8),
+        # x (each token once), packed gate|up weights, H written
+        "gemm_gate_up": (2 * S * d * 2 * h, T * d * es + E * 2 * h * d * es + S * h * es),
+        # H read, down weights, y_sorted written
+        "gemm_down": (2 * S * h * d, S * h * es + E * h * d * es + S * d * es),
         # y_sorted and shared_out read, combine weights and slot map read, out written
-        "combine": ("byte", S * d * es + S * 8 + T * d * es * (2 if hs else 1)),
+        "combine": (0, S * d * es + S * 8 + T * d * es * (2 if hs else 1)),
         # expert indices read twice (count, scatter), perm and inv_perm written
-        "permute_scatter": ("byte", S * 4 * 3),
+        "permute_scatter": (0, S * 4 * 3),
     }
     if hs:
-        w["shared_gate_up"] = ("flop", 2 * T * d * 2 * hs)
-        w["shared_down"] = ("flop", 2 * T * hs * d)
+        w["shared_gate_up"] = (2 * T * d * 2 * hs, T * d * es + 2 * hs * d * es + T * hs * es)
+        w["shared_down"] = (2 * T * hs * d, T * hs * es + hs * d * es + T * d * es)
     return w
 
 
-def roofline_of(kname, kind, amount, avg_ms, dtype):
-    if kind == "byte":
-        ach = amount / (avg_ms * 1e-3) / 1e9
-        return {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": ach / PEAK_HBM_GBS}
-    ach = amount / (avg_ms * 1e-3) / 1e12
+def roofline_of(kname, flops, nbytes, avg_ms, dtype):
+    """Roofline position of one launch: the bound is whichever of compute
+    (MFMA, or fp32 VALU for the router) and HBM takes longer at peak."""
+    t = avg_ms * 1e-3
     if kname == "route":
-        return {"kernel": kname, "bound": "alu", "achieved": ach, "peak": PEAK_VALU_TFLOPS,
-                "unit": "TFLOP/s", "frac": ach / PEAK_VALU_TFLOPS}
-    peak = PEAK_TFLOPS[dtype]
-    return {"kernel": kname, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
-            "frac": ach / peak}
+        cpeak, cunit, cbound = PEAK_VALU_TFLOPS, "TFLOP/s", "alu"
+    else:
+        cpeak, cunit, cbound = PEAK_TFLOPS[dtype], "TFLOP/s", "mfma"
+    t_compute = flops / (cpeak * 1e12)
+    t_mem = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_compute >= t_mem:
+        ach = flops / t / 1e12
+        return {"kernel": kname, "bound": cbound, "achieved": ach, "peak": cpeak, "unit": cunit,
+                "frac": ach / cpeak}
+    ach = nbytes / t / 1e9
+    return {"kernel": kname, "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS}
 
 
 def trace_name(kernel):
     """libmoe trace name of a compiled forward kernel, from its signature."""
     import re
-    if "route_kernel" in kernel:
+    if "route_kernel" in kernel or "route_resident_kernel" in kernel:
         return "route"
     if "combine_kernel" in kernel:
         return "combine"
@@ -87,7 +96,8 @@ def trace_name(kernel):
             return f"permute_{k}"
     if "pack_kernel" in kernel:
         return "pack_weights"
-    m = re.search(r"gemm_kernel<[^>]*>, (true|false), (\d), (true|false)>", kernel)
+    m = (re.search(r"wide_gemm_kernel<(true|false), (\d), (true|false)>", kernel) or
+         re.search(r"gemm_kernel<[^>]*>, (true|false), (\d), (true|false)>", kernel))
     if m:
         gather, epi, dense = m.group(1) == "true", int(m.group(2)), m.group(3) == "true"
         if dense:
@@ -277,8 +287,8 @@ def main():
             pass
     peak = PEAK_TFLOPS[p.dtype]
     routed_ms = sum(avg[k] for k in ("gemm_gate_up", "gemm_down") if k in avg)
-    routed_fl = wk["gemm_gate_up"][1] + wk["gemm_down"][1]
-    total_fl = sum(v[1] for k, v in wk.items() if v[0] == "flop")
+    routed_fl = wk["gemm_gate_up"][0] + wk["gemm_down"][0]
+    total_fl = sum(v[0] for v in wk.values())
     line = {
         "metric": "dropless MoE fwd tokens/s + grouped-GEMM % MFMA peak (E=64 top-8, 131k tok)",
         "value": p.tokens / (ms * 1e-3),
