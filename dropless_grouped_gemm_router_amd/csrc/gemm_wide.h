@@ -73,10 +73,17 @@ __device__ __forceinline__ void wide_issue(char* buf, const char* const (&a_row)
                                      16, 0, 0);
 }
 
-// Multiply one stage out of LDS: four 16-element K steps.
-__device__ __forceinline__ void wide_compute(const char* buf, int a_frag, int b_frag,
-                                             const int (&sw)[4],
+// Multiply one stage out of LDS: four 16-element K steps. K step q reads
+// chunk 2q + g of its rows at position (2q + g) ^ ((r32 >> 1) & 7), i.e.
+// 2q ^ sw_base with sw_base = g ^ ((r32 >> 1) & 7); the positions are formed
+// per call (an opaque copy of the base) instead of held in registers.
+__device__ __forceinline__ void wide_compute(const char* buf, int a_frag, int b_frag, int sw_base,
                                              f32x16_t (&acc)[WideCfg::WM_SUB][WideCfg::WN_SUB]) {
+  int sb = sw_base;
+  asm volatile("" : "+v"(sb));
+  int sw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sw[q] = ((2 * q) ^ sb) << 4;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     u32x4 xf[WideCfg::WM_SUB], wf[WideCfg::WN_SUB];
@@ -287,9 +294,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
   // the swizzled position of K step q's chunk 2 q + g.
   const int a_frag = (wm * WideCfg::WM_SUB * 32 + r32) * kWideRowBytes;
   const int b_frag = (256 + wn * WideCfg::WN_SUB * 32 + r32) * kWideRowBytes;
-  int sw[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) sw[q] = ((2 * q + g) ^ ((r32 >> 1) & 7)) << 4;
+  const int sw_base = g ^ ((r32 >> 1) & 7);
 
   TileInfo cur = wide_tile<kDense>(p, tiles, num_tiles, w, n_tiles_n);
   if (cur.rows <= 0) return;
@@ -338,7 +343,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
         nxt = (w1 < w_end) ? wide_tile<kDense>(p, tiles, num_tiles, w1, n_tiles_n) : TileInfo{0, 0, 0};
         wide_src_rows<kGather>(p, nxt, lrow, src);
       }
-      wide_compute(smem + buf * kWideStage, a_frag, b_frag, sw, acc);
+      wide_compute(smem + buf * kWideStage, a_frag, b_frag, sw_base, acc);
       buf ^= 1;
     }
 

@@ -39,6 +39,8 @@ SMALL = [
     Problem(1000, 64, 8, 128, 64, 64, "bf16", 128),
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256),
     Problem(700, 4, 2, 256, 256, 0, "fp32", 256),
+    # bf16, block_m 256, three 256-column tiles of d_model in the down GEMM
+    Problem(900, 16, 4, 768, 128, 0, "bf16", 256),
 ]
 
 
@@ -61,8 +63,10 @@ def test_forward_small_elementwise(p):
     assert np.all(np.isfinite(to_np(out)))
 
 
-def test_forward_deterministic():
-    p = Problem(777, 8, 2, 256, 128, 128, "bf16", 64)
+@pytest.mark.parametrize("p", [Problem(777, 8, 2, 256, 128, 128, "bf16", 64),
+                               Problem(2000, 8, 2, 512, 128, 128, "bf16", 256)],
+                         ids=["bm64", "bm256"])
+def test_forward_deterministic(p):
     c = Case(p, seed=3)
     a = c.forward().clone()
     ya = c.buf.y_sorted.clone()
