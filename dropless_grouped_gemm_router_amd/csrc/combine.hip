@@ -3,7 +3,8 @@
 // as a gather-sum: one wave owns one output row, reads its k sorted expert
 // rows, accumulates in fp32 in rank order i = 0..k-1 and writes the row
 // once. No atomics, so the result is deterministic. The stage is bound by
-// HBM bandwidth: each lane moves 16-byte pieces of a row.
+// HBM bandwidth: each lane moves 16-byte pieces of a row. k <= 8 takes a
+// variant with all row loads of a piece in flight at once.
 #include "common.h"
 
 namespace moe {
@@ -41,6 +42,48 @@ struct Vec<float> {
   }
 };
 
+// k = K <= 8: lane i reads slot i's row index and weight (one coalesced
+// load each), the wave broadcasts them, and all K row loads of a 16-byte
+// piece (and the shared row's) are issued before any is used, so a token
+// costs one memory latency instead of 2K dependent ones. Accumulation is
+// still in rank order.
+template <typename T, bool kShared, int K>
+__global__ __launch_bounds__(kCombThreads) void combine_k_kernel(
+    int64_t ntok, int d, const T* __restrict__ y, const float* __restrict__ w,
+    const int32_t* __restrict__ inv_perm, const T* __restrict__ shared_out, T* __restrict__ out) {
+  constexpr int N = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kCombThreads / 64) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int my_row = lane < K ? inv_perm[t * K + lane] : 0;
+  const float my_w = lane < K ? w[t * K + lane] : 0.0f;
+  int64_t row[K];
+  float wi[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    row[i] = __builtin_amdgcn_readlane(my_row, i);
+    wi[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), i));
+  }
+  for (int c = lane * N; c < d; c += 64 * N) {
+    float v[K][N], sv[N];
+#pragma unroll
+    for (int i = 0; i < K; ++i) Vec<T>::load(y + row[i] * d + c, v[i]);
+    if (kShared) Vec<T>::load(shared_out + t * d + c, sv);
+    float acc[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] = __builtin_fmaf(wi[i], v[i][q], acc[q]);
+    if (kShared) {
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += sv[q];
+    }
+    Vec<T>::store(out + t * d + c, acc);
+  }
+}
+
 template <typename T, bool kShared>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int64_t ntok, int k, int d, const T* __restrict__ y, const float* __restrict__ w,
@@ -71,10 +114,36 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
   }
 }
 
+template <typename T, int K>
+hipError_t launch_combine_k(int64_t T_, int d, const void* y, const float* w, const int32_t* inv,
+                            const void* sh, void* out, int64_t blocks, hipStream_t s) {
+  if (sh)
+    MOE_LAUNCH("combine", (combine_k_kernel<T, true, K>), dim3(static_cast<unsigned>(blocks)),
+               dim3(kCombThreads), 0, s, T_, d, static_cast<const T*>(y), w, inv,
+               static_cast<const T*>(sh), static_cast<T*>(out));
+  else
+    MOE_LAUNCH("combine", (combine_k_kernel<T, false, K>), dim3(static_cast<unsigned>(blocks)),
+               dim3(kCombThreads), 0, s, T_, d, static_cast<const T*>(y), w, inv,
+               static_cast<const T*>(nullptr), static_cast<T*>(out));
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_combine_t(int64_t T_, int k, int d, const void* y, const float* w,
                             const int32_t* inv, const void* sh, void* out, hipStream_t s) {
   const int64_t blocks = (T_ + kCombThreads / 64 - 1) / (kCombThreads / 64);
+  if (k <= 8) {
+    switch (k) {
+      case 1: return launch_combine_k<T, 1>(T_, d, y, w, inv, sh, out, blocks, s);
+      case 2: return launch_combine_k<T, 2>(T_, d, y, w, inv, sh, out, blocks, s);
+      case 3: return launch_combine_k<T, 3>(T_, d, y, w, inv, sh, out, blocks, s);
+      case 4: return launch_combine_k<T, 4>(T_, d, y, w, inv, sh, out, blocks, s);
+      case 5: return launch_combine_k<T, 5>(T_, d, y, w, inv, sh, out, blocks, s);
+      case 6: return launch_combine_k<T, 6>(T_, d, y, w, inv, sh, out, blocks, s);
+      case 7: return launch_combine_k<T, 7>(T_, d, y, w, inv, sh, out, blocks, s);
+      default: return launch_combine_k<T, 8>(T_, d, y, w, inv, sh, out, blocks, s);
+    }
+  }
   if (sh)
     MOE_LAUNCH("combine", (combine_kernel<T, true>), dim3(static_cast<unsigned>(blocks)),
                        dim3(kCombThreads), 0, s, T_, k, d, static_cast<const T*>(y), w, inv,
