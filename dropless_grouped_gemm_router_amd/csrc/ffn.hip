@@ -19,36 +19,49 @@ namespace {
 
 constexpr int kPackTile = 64;
 
-// dst[g][p][k] (K contiguous) from src[g][k][n] (N contiguous).
+// dst[g][p][k] (K contiguous) from src[g][k][n] (N contiguous), one 64 x 64
+// tile per workgroup, 16-byte loads and stores around an LDS transpose.
 // interleave == 0: p = n of src0. interleave != 0: dst has 2 * nsrc rows;
 // row p takes column 16 * (p / 32) + p % 16 of src0 (gate) when p % 32 < 16,
-// else the same column of src1 (up).
+// else the same column of src1 (up). So the 64 rows of a tile come from four
+// runs of 16 consecutive source columns: gate, up, gate, up.
 template <typename T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src0,
                                                    const T* __restrict__ src1, T* __restrict__ dst,
                                                    int K, int nsrc, int interleave) {
-  __shared__ T tile[kPackTile][kPackTile + 1];
+  constexpr int V = 16 / static_cast<int>(sizeof(T));  // elements per 16 bytes
+  __shared__ T tile[kPackTile][kPackTile + 2];          // [k][p]
   const int ndst = interleave ? 2 * nsrc : nsrc;
   const int p0 = blockIdx.x * kPackTile, k0 = blockIdx.y * kPackTile;
   const int64_t gs = static_cast<int64_t>(K) * nsrc;
   const T* s0 = src0 + blockIdx.z * gs;
   const T* s1 = interleave ? src1 + blockIdx.z * gs : s0;
-  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
-    const int kk = i / kPackTile, pp = i % kPackTile;
-    const int pr = p0 + pp;
+  // Load: piece (kk, c) = 16 bytes of row k0 + kk at tile rows c*V .. c*V + V-1.
+  constexpr int kPieces = kPackTile / V;
+  for (int i = threadIdx.x; i < kPackTile * kPieces; i += 256) {
+    const int kk = i / kPieces, c = (i % kPieces) * V;
+    const int pr = p0 + c;
     const T* s = s0;
     int col = pr;
     if (interleave) {
       col = 16 * (pr / 32) + pr % 16;
       if (pr % 32 >= 16) s = s1;
     }
-    tile[pp][kk] = s[static_cast<int64_t>(k0 + kk) * nsrc + col];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(s + static_cast<int64_t>(k0 + kk) * nsrc + col);
+    const T* e = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int q = 0; q < V; ++q) tile[kk][c + q] = e[q];
   }
   __syncthreads();
+  // Store: piece (pp, c) = 16 bytes of dst row p0 + pp at k0 + c*V.
   T* d = dst + blockIdx.z * static_cast<int64_t>(ndst) * K;
-  for (int i = threadIdx.x; i < kPackTile * kPackTile; i += 256) {
-    const int pp = i / kPackTile, kk = i % kPackTile;
-    d[static_cast<int64_t>(p0 + pp) * K + k0 + kk] = tile[pp][kk];
+  for (int i = threadIdx.x; i < kPackTile * kPieces; i += 256) {
+    const int pp = i / kPieces, c = (i % kPieces) * V;
+    u32x4 v;
+    T* e = reinterpret_cast<T*>(&v);
+#pragma unroll
+    for (int q = 0; q < V; ++q) e[q] = tile[c + q][pp];
+    *reinterpret_cast<u32x4*>(d + static_cast<int64_t>(p0 + pp) * K + k0 + c) = v;
   }
 }
 

@@ -60,8 +60,23 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   const int64_t L = static_cast<int64_t>(E) * nblk;
   const int64_t chunk = (L + kScanThreads - 1) / kScanThreads;
   const int64_t b0 = min(L, chunk * threadIdx.x), b1 = min(L, b0 + chunk);
+  // Up to kScanRegs entries per thread are read once, all loads in flight
+  // together, and kept in registers for the write-back.
+  constexpr int kScanRegs = 16;
+  const bool in_regs = chunk <= kScanRegs;
+  int32_t vals[kScanRegs];
   int32_t local = 0;
-  for (int64_t i = b0; i < b1; ++i) local += blk_counts[i];
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < kScanRegs; ++q) {
+      const int64_t i = b0 + q;
+      const int32_t v = blk_counts[i < L ? i : L - 1];
+      vals[q] = i < b1 ? v : 0;
+      local += vals[q];
+    }
+  } else {
+    for (int64_t i = b0; i < b1; ++i) local += blk_counts[i];
+  }
   // Exclusive scan of the per-thread sums: within the wave, then across waves.
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t incl = local;
@@ -82,11 +97,23 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   }
   __syncthreads();
   int32_t run = wsum[wave] + incl - local;
-  for (int64_t i = b0; i < b1; ++i) {
-    const int32_t v = blk_counts[i];
-    blk_counts[i] = run;
-    if (i % nblk == 0) off[i / nblk] = run;  // block 0 of expert i / nblk
-    run += v;
+  if (in_regs) {
+#pragma unroll
+    for (int q = 0; q < kScanRegs; ++q) {
+      const int64_t i = b0 + q;
+      if (i < b1) {
+        blk_counts[i] = run;
+        if (i % nblk == 0) off[i / nblk] = run;  // block 0 of expert i / nblk
+        run += vals[q];
+      }
+    }
+  } else {
+    for (int64_t i = b0; i < b1; ++i) {
+      const int32_t v = blk_counts[i];
+      blk_counts[i] = run;
+      if (i % nblk == 0) off[i / nblk] = run;
+      run += v;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
