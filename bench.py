@@ -208,6 +208,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="index into inputs.WORKLOADS")
     ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--skew", type=float, default=0.0,
+                    help="routing skew of the synthetic router (inputs.Problem.skew)")
     ap.add_argument("--cpu-sample", type=int, default=131072,
                     help="tokens the CPU oracle runs on (about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -247,6 +249,8 @@ def main():
     name, p, _ = WORKLOADS[args.workload]
     if args.block_m:
         p = dataclasses.replace(p, block_m=args.block_m)
+    if args.skew:
+        p = dataclasses.replace(p, skew=args.skew)
     torch.cuda.set_device(0)
     print(f"bench: {name} bm={p.block_m}: generating inputs", file=sys.stderr, flush=True)
     inputs = make_inputs(p, seed=0)
@@ -304,7 +308,7 @@ def main():
         "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, uniform routing",
         "config": {"workload": name, "tokens": p.tokens, "experts": p.experts, "top_k": p.top_k,
                    "d_model": p.d_model, "d_hidden": p.d_hidden, "d_shared": p.d_shared,
-                   "block_m": p.block_m},
+                   "block_m": p.block_m, "skew": p.skew},
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
         "roofline": roof,

@@ -6,8 +6,9 @@ the layer's arithmetic lives here.
 
 The benchmark pages (probjax ``kernel_gmm_gpu.json``, ``gpu_nn.json`` and
 ``gpu_moe_h100.json``) run on seeded Gaussian tokens with uniform routing
-(``skew`` 0.0 in every ``config.sources[*].config`` block) and print neither
-seeds nor a generator, so the generator is defined here:
+(``skew`` 0.0 in every ``config.sources[*].config`` block; the pages also
+name a skew of 0.9 without defining it, see ``Problem.skew``) and print
+neither seeds nor a generator, so the generator is defined here:
 
 * SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
   generators", OOPSLA 2014) used counter-style: draw ``i`` of a stream with
@@ -123,6 +124,9 @@ class Problem:
     d_shared: int = 0
     dtype: str = "bf16"  # "fp32" or "bf16": storage dtype of x, expert weights, activations
     block_m: int = 128
+    # Routing skew of the generated router (0 = uniform routing). Not a layer
+    # argument: it only shapes the synthetic router, see make_inputs.
+    skew: float = 0.0
 
     @property
     def slots(self) -> int:
@@ -172,6 +176,16 @@ def make_inputs(p: Problem, seed: int = 0, with_grad_out: bool = False,
         if names is not None and name not in names:
             continue
         out[name] = gen_tensor(seed, name, shape, std, dt)
+    if p.skew > 0.0 and "w_router" in out:
+        # Skewed routing: expert e's router column is scaled by
+        # (1 - skew)^(e / (E - 1)), so its logits have standard deviation
+        # falling from 1 (expert 0) to 1 - skew (expert E - 1) and top-k picks
+        # low-index experts more often (skew 0.9 at E=64, k=8: the busiest
+        # expert gets about 2.7 times the mean load). At skew 0 nothing changes.
+        e = np.arange(E, dtype=np.float64)
+        scale = ((1.0 - p.skew) ** (e / max(E - 1, 1))).astype(np.float32)
+        f = (out["w_router"].stored * scale[None, :]).astype(np.float32)
+        out["w_router"] = Tensor(stored=f, value=f)
     return out
 
 

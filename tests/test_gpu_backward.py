@@ -49,10 +49,11 @@ SMALL = [
     Problem(1000, 64, 8, 128, 128, 256, "bf16", 128),
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256),
     Problem(700, 4, 2, 256, 256, 128, "fp32", 256),
+    Problem(2000, 64, 8, 256, 128, 128, "bf16", 128, skew=0.9),
 ]
 
 
-@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}")
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}" + (f"skew{p.skew}" if p.skew else ""))
 def test_backward_small_elementwise(p):
     note(f"backward small {p}")
     c = Case(p, seed=11, training=True)

@@ -41,10 +41,13 @@ SMALL = [
     Problem(700, 4, 2, 256, 256, 0, "fp32", 256),
     # bf16, block_m 256, three 256-column tiles of d_model in the down GEMM
     Problem(900, 16, 4, 768, 128, 0, "bf16", 256),
+    # skewed routing (uneven expert loads, nearly empty experts)
+    Problem(3000, 64, 8, 256, 128, 128, "bf16", 256, skew=0.9),
+    Problem(3000, 64, 8, 256, 128, 0, "bf16", 64, skew=0.9),
 ]
 
 
-@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}")
+@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}" + (f"skew{p.skew}" if p.skew else ""))
 def test_forward_small_elementwise(p):
     note(f"forward small {p}")
     c = Case(p, seed=7)

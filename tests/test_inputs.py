@@ -37,3 +37,32 @@ def test_init_scales_and_storage():
     assert abs(t["w_down"].value.std() * np.sqrt(64) - 1) < 0.05
     assert abs(t["ws_down"].value.std() * np.sqrt(128) - 1) < 0.05
     assert np.array_equal(inputs.bf16_bits_to_f32(t["x"].stored), t["x"].value)
+
+
+def test_skew_zero_is_the_uniform_router_and_skew_scales_columns():
+    p0 = inputs.Problem(256, 64, 8, 256, 64, 0, "bf16", 128)
+    p9 = inputs.Problem(256, 64, 8, 256, 64, 0, "bf16", 128, skew=0.9)
+    a = inputs.make_inputs(p0, seed=3)
+    b = inputs.make_inputs(inputs.Problem(256, 64, 8, 256, 64, 0, "bf16", 128, skew=0.0), seed=3)
+    c = inputs.make_inputs(p9, seed=3)
+    for n in a:
+        assert np.array_equal(a[n].stored, b[n].stored), n
+        if n != "w_router":
+            assert np.array_equal(a[n].stored, c[n].stored), n
+    # column e scaled by 0.1^(e/63): expert 0 unchanged, expert 63 by 0.1
+    ratio = c["w_router"].value / a["w_router"].value
+    assert np.allclose(ratio[:, 0], 1.0) and np.allclose(ratio[:, 63], 0.1, rtol=1e-6)
+    assert np.allclose(ratio[:, 21], 0.1 ** (21 / 63), rtol=1e-6)
+
+
+def test_skewed_routing_loads_low_experts():
+    """Plausibility: at skew 0.9 the busiest expert carries well over twice
+    the mean load, at skew 0 it stays near the mean."""
+    from oracle import oracle
+
+    for skew, lo, hi in ((0.0, 1.0, 1.5), (0.9, 2.0, 4.0)):
+        p = inputs.Problem(4096, 64, 8, 512, 64, 0, "fp32", 128, skew=skew)
+        t = inputs.make_inputs(p, seed=0, names=["x", "w_router"])
+        _, idx, _ = oracle.route(t["x"].value, t["w_router"].value, p.top_k)
+        frac = np.bincount(idx.ravel(), minlength=64).max() / idx.size
+        assert lo < frac * 64 < hi, (skew, frac * 64)
