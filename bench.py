@@ -40,28 +40,36 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def work(p):
+def work(p, dispatch="gather"):
     """Algorithmic work of each forward kernel per launch: (flops, bytes).
     FLOPs count a multiply-add as 2; bytes are the minimum each kernel must
     move through HBM (each input read once, each output written once)."""
     T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
     S = T * k
     es = 2 if p.dtype == "bf16" else 4
+    # the gate/up GEMM reads each token once, or (sorted) the expert-ordered copy
+    a_rows = S if dispatch == "sorted" else T
     w = {
         # x and the router read, indices and weights written
         "route": (2 * T * d * E, T * d * es + d * E * 4 + S * 8),
-        # x (each token once), packed gate|up weights, H written
-        "gemm_gate_up": (2 * S * d * 2 * h, T * d * es + E * 2 * h * d * es + S * h * es),
+        # tokens, packed gate|up weights, H written
+        "gemm_gate_up": (2 * S * d * 2 * h, a_rows * d * es + E * 2 * h * d * es + S * h * es),
         # H read, down weights, y_sorted written
         "gemm_down": (2 * S * h * d, S * h * es + E * h * d * es + S * d * es),
         # y_sorted and shared_out read, combine weights and slot map read, out written
         "combine": (0, S * d * es + S * 8 + T * d * es * (2 if hs else 1)),
         # expert indices read twice (count, scatter), perm and inv_perm written
         "permute_scatter": (0, S * 4 * 3),
+        # tokens read once, perm read, the expert-ordered copy written
+        "sort_rows": (0, T * d * es + S * 4 + S * d * es),
     }
     if hs:
         w["shared_gate_up"] = (2 * T * d * 2 * hs, T * d * es + 2 * hs * d * es + T * hs * es)
         w["shared_down"] = (2 * T * hs * d, T * hs * es + hs * d * es + T * d * es)
+        # shared down GEMM with the gather-sum in its epilogue: y_sorted,
+        # weights and slot map read, out written (no shared_out round trip)
+        w["shared_down_combine"] = (2 * T * hs * d,
+                                    T * hs * es + hs * d * es + S * d * es + S * 8 + T * d * es)
     return w
 
 
@@ -96,12 +104,14 @@ def trace_name(kernel):
             return f"permute_{k}"
     if "pack_kernel" in kernel:
         return "pack_weights"
+    if "sort_rows_kernel" in kernel:
+        return "sort_rows"
     m = (re.search(r"wide_gemm_kernel<(true|false), (\d), (true|false)>", kernel) or
          re.search(r"gemm_kernel<[^>]*>, (true|false), (\d), (true|false)>", kernel))
     if m:
         gather, epi, dense = m.group(1) == "true", int(m.group(2)), m.group(3) == "true"
         if dense:
-            return "shared_gate_up" if epi == 1 else "shared_down"
+            return {1: "shared_gate_up", 3: "shared_down_combine"}.get(epi, "shared_down")
         return "gemm_gate_up" if epi == 1 else "gemm_down"
     return None
 
@@ -208,6 +218,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3, help="index into inputs.WORKLOADS")
     ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--dispatch", choices=["gather", "sorted", "fused_gsum"], default="gather",
+                    help="forward dispatch variant (moe_forward)")
     ap.add_argument("--skew", type=float, default=0.0,
                     help="routing skew of the synthetic router (inputs.Problem.skew)")
     ap.add_argument("--cpu-sample", type=int, default=131072,
@@ -255,13 +267,13 @@ def main():
     print(f"bench: {name} bm={p.block_m}: generating inputs", file=sys.stderr, flush=True)
     inputs = make_inputs(p, seed=0)
     dev = B.device_inputs(inputs, "cuda:0")
-    buf = B.allocate(p, "cuda:0")
+    buf = B.allocate(p, "cuda:0", dispatch=args.dispatch)
     x = dev.pop("x")
     w = dev
     torch.cuda.synchronize()
 
     def step():
-        B.forward(p, x, w, buf)
+        B.forward_dispatch(p, args.dispatch, x, w, buf)
 
     for _ in range(args.warmup):
         step()
@@ -273,7 +285,7 @@ def main():
     kern = B.moe_trace_summary()
     B.moe_trace_enable(False)
 
-    wk = work(p)
+    wk = work(p, args.dispatch)
     per_step = {k: v["ms"] / args.steps for k, v in kern.items()}
     avg = {k: v["ms"] / v["count"] for k, v in kern.items()}
     dom = max(per_step, key=per_step.get)
@@ -292,7 +304,7 @@ def main():
     peak = PEAK_TFLOPS[p.dtype]
     routed_ms = sum(avg[k] for k in ("gemm_gate_up", "gemm_down") if k in avg)
     routed_fl = wk["gemm_gate_up"][0] + wk["gemm_down"][0]
-    total_fl = sum(v[0] for v in wk.values())
+    total_fl = sum(wk[k][0] for k in avg if k in wk)
     line = {
         "metric": "dropless MoE fwd tokens/s + grouped-GEMM % MFMA peak (E=64 top-8, 131k tok)",
         "value": p.tokens / (ms * 1e-3),
@@ -305,10 +317,11 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": p.dtype,
-        "data": "synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, uniform routing",
+        "data": ("synthetic: seeded N(0,1) tokens, N(0,1/fan_in) weights, "
+                 + ("unskewed random router" if not p.skew else f"router skew {p.skew}")),
         "config": {"workload": name, "tokens": p.tokens, "experts": p.experts, "top_k": p.top_k,
                    "d_model": p.d_model, "d_hidden": p.d_hidden, "d_shared": p.d_shared,
-                   "block_m": p.block_m, "skew": p.skew},
+                   "block_m": p.block_m, "skew": p.skew, "dispatch": args.dispatch},
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
         "roofline": roof,

@@ -20,6 +20,9 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_FP32, MOE_BF16 = 0, 1
 DTYPES = {"fp32": MOE_FP32, "bf16": MOE_BF16}
+MOE_DISPATCH_GATHER, MOE_DISPATCH_SORTED, MOE_DISPATCH_FUSED_GSUM = 0, 1, 2
+DISPATCH = {"gather": MOE_DISPATCH_GATHER, "sorted": MOE_DISPATCH_SORTED,
+            "fused_gsum": MOE_DISPATCH_FUSED_GSUM}
 
 
 class MoeError(RuntimeError):
@@ -52,8 +55,8 @@ class moe_grads(ctypes.Structure):
 
 EXPORTED = ["moe_version", "moe_status_string", "moe_check_problem", "moe_max_tiles",
             "moe_param_count", "moe_workspace_bytes", "moe_saved_bytes", "moe_route",
-            "moe_permute", "moe_ffn_fwd", "moe_combine", "moe_bwd", "moe_trace_enable",
-            "moe_trace_summary"]
+            "moe_permute", "moe_ffn_fwd", "moe_combine", "moe_forward_workspace_bytes",
+            "moe_forward", "moe_bwd", "moe_trace_enable", "moe_trace_summary"]
 
 _lib = None
 
@@ -81,6 +84,10 @@ def load(path: str = LIB_PATH):
         "moe_ffn_fwd": (ctypes.c_int, [PP, P, ctypes.POINTER(moe_weights),
                                        ctypes.POINTER(moe_routing), P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [PP, P, ctypes.POINTER(moe_routing), P, P, P]),
+        "moe_forward_workspace_bytes": (ctypes.c_size_t, [PP, ctypes.c_int, ctypes.c_int]),
+        "moe_forward": (ctypes.c_int, [PP, ctypes.c_int, P, ctypes.POINTER(moe_weights),
+                                       ctypes.POINTER(moe_routing), P, P, P, P, ctypes.c_size_t,
+                                       P]),
         "moe_bwd": (ctypes.c_int, [PP, P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing),
                                    P, P, P, P, ctypes.POINTER(moe_grads), P, ctypes.c_size_t, P]),
         "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -198,6 +205,24 @@ def moe_combine(p, y_sorted, routing: Dict, shared_out, out, stream=None):
                               _ptr(shared_out), _ptr(out), _stream(stream)), "moe_combine")
 
 
+def _dispatch(dispatch) -> int:
+    return DISPATCH[dispatch] if isinstance(dispatch, str) else int(dispatch)
+
+
+def moe_forward_workspace_bytes(p, dispatch, training: bool = False) -> int:
+    return int(load().moe_forward_workspace_bytes(ctypes.byref(problem_struct(p)),
+                                                  _dispatch(dispatch), int(training)))
+
+
+def moe_forward(p, dispatch, x, weights: Dict, routing: Dict, y_sorted, saved, out, workspace,
+                workspace_bytes: Optional[int] = None, stream=None):
+    w, r = weights_struct(weights), routing_struct(routing)
+    nb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    _check(load().moe_forward(ctypes.byref(problem_struct(p)), _dispatch(dispatch), _ptr(x),
+                              ctypes.byref(w), ctypes.byref(r), _ptr(y_sorted), _ptr(saved),
+                              _ptr(out), _ptr(workspace), nb, _stream(stream)), "moe_forward")
+
+
 def moe_bwd(p, x, weights: Dict, routing: Dict, y_sorted, saved, grad_out, grad_x, grads: Dict,
             workspace, workspace_bytes: Optional[int] = None, stream=None):
     w, r, g = weights_struct(weights), routing_struct(routing), grads_struct(grads)
@@ -241,7 +266,9 @@ def torch_dtype(p):
     return torch.bfloat16 if (p.dtype == "bf16" or p.dtype == MOE_BF16) else torch.float32
 
 
-def allocate(p, device="cuda", training: bool = False) -> Buffers:
+def allocate(p, device="cuda", training: bool = False, dispatch=None) -> Buffers:
+    """Buffers for the staged calls; with ``dispatch`` the workspace also
+    covers moe_forward with that variant."""
     import torch
     T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
     S = T * k
@@ -256,7 +283,10 @@ def allocate(p, device="cuda", training: bool = False) -> Buffers:
         tiles=torch.empty((max(1, moe_max_tiles(p)), 3), **i32),
         num_tiles=torch.empty(1, **i32),
     )
-    ws = torch.empty(moe_workspace_bytes(p, training), dtype=torch.uint8, device=device)
+    nws = moe_workspace_bytes(p, training)
+    if dispatch is not None:
+        nws = max(nws, moe_forward_workspace_bytes(p, dispatch, training))
+    ws = torch.empty(nws, dtype=torch.uint8, device=device)
     b = Buffers(routing=routing,
                 y_sorted=torch.empty((S, d), dtype=dt, device=device),
                 shared_out=torch.empty((T, d), dtype=dt, device=device) if hs else None,
@@ -281,6 +311,15 @@ def forward(p, x, weights: Dict, buf: Buffers, training: bool = False, stream=No
     moe_ffn_fwd(p, x, weights, buf.routing, buf.y_sorted, buf.shared_out,
                 buf.saved if training else None, buf.workspace, stream=stream)
     moe_combine(p, buf.y_sorted, buf.routing, buf.shared_out, buf.out, stream)
+    return buf.out
+
+
+def forward_dispatch(p, dispatch, x, weights: Dict, buf: Buffers, training: bool = False,
+                     stream=None):
+    """The whole forward in one moe_forward call with a dispatch variant
+    (buf from ``allocate(..., dispatch=...)``); returns buf.out."""
+    moe_forward(p, dispatch, x, weights, buf.routing, buf.y_sorted,
+                buf.saved if training else None, buf.out, buf.workspace, stream=stream)
     return buf.out
 
 

@@ -141,6 +141,34 @@ MOE_EXPORT int moe_combine(const moe_problem* p, const void* y_sorted, const moe
                                         as_stream(stream)));
 }
 
+MOE_EXPORT size_t moe_forward_workspace_bytes(const moe_problem* p, int dispatch, int training) {
+  if (check(p) != MOE_OK) return 0;
+  if (dispatch < MOE_DISPATCH_GATHER || dispatch > MOE_DISPATCH_FUSED_GSUM) return 0;
+  return moe::forward_layout(*p, dispatch, training != 0).total;
+}
+
+MOE_EXPORT int moe_forward(const moe_problem* p, int dispatch, const void* x, const moe_weights* w,
+                           moe_routing* r, void* y_sorted, void* saved, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (dispatch < MOE_DISPATCH_GATHER || dispatch > MOE_DISPATCH_FUSED_GSUM) return MOE_ERR_INVALID;
+  int st = check(p);
+  if (st != MOE_OK) return st;
+  if (p->tokens == 0) return MOE_OK;
+  if (!w || !r || !ok_ptr(x) || !ok_ptr(w->w_router, 4) || !ok_ptr(w->w_gate) || !ok_ptr(w->w_up) ||
+      !ok_ptr(w->w_down) || !ok_ptr(r->topk_idx, 4) || !ok_ptr(r->topk_w, 4) ||
+      !ok_ptr(r->expert_offsets, 4) || !ok_ptr(r->perm, 4) || !ok_ptr(r->inv_perm, 4) ||
+      !ok_ptr(r->tiles, 4) || !ok_ptr(r->num_tiles, 4) || !ok_ptr(y_sorted) || !ok_ptr(out) ||
+      !ok_ptr(workspace, 256))
+    return MOE_ERR_INVALID;
+  if (p->d_shared > 0 && (!ok_ptr(w->ws_gate) || !ok_ptr(w->ws_up) || !ok_ptr(w->ws_down)))
+    return MOE_ERR_INVALID;
+  if (saved && !aligned(saved, 256)) return MOE_ERR_INVALID;
+  if (workspace_bytes < moe::forward_layout(*p, dispatch, saved != nullptr).total)
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_forward(*p, dispatch, x, *w, *r, y_sorted, saved, out, workspace,
+                                        as_stream(stream)));
+}
+
 MOE_EXPORT int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w,
                        const moe_routing* r, const void* y_sorted, const void* saved,
                        const void* grad_out, void* grad_x, const moe_grads* g, void* workspace,

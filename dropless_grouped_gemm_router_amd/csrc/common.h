@@ -139,6 +139,18 @@ hipError_t launch_ffn_fwd(const moe_problem& p, const void* x, const moe_weights
                           const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
                           void* ws, hipStream_t s);
 
+// Whole forward (moe_forward): workspace offsets (bytes) of the staged
+// shared-expert output and of the expert-ordered token copy, after the
+// permute/FFN area at offset 0.
+struct ForwardLayout {
+  size_t shared_out, x_sorted, total;
+  bool fused;  // the combine runs in the shared down GEMM's epilogue
+};
+ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training);
+hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, const moe_weights& w,
+                          const moe_routing& r, void* y_sorted, void* saved, void* out, void* ws,
+                          hipStream_t s);
+
 size_t bwd_ws_bytes(const moe_problem& p);
 hipError_t launch_bwd(const moe_problem& p, const void* x, const moe_weights& w,
                       const moe_routing& r, const void* y_sorted, const void* saved,

@@ -76,14 +76,41 @@ void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc
 
 
 
+// Dispatch "sorted": token rows copied into expert order before the
+// gate/up GEMM, x_sorted[j] = x[perm[j] / k]. One wave per row, 16-byte
+// pieces.
+template <typename T>
+__global__ __launch_bounds__(256) void sort_rows_kernel(const T* __restrict__ x,
+                                                        const int32_t* __restrict__ perm, int k,
+                                                        int64_t S, int d, T* __restrict__ xs) {
+  constexpr int V = 16 / static_cast<int>(sizeof(T));
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (j >= S) return;
+  const int64_t t = perm[j] / k;
+  for (int c = (threadIdx.x & 63) * V; c < d; c += 64 * V)
+    *reinterpret_cast<u32x4*>(xs + j * d + c) = *reinterpret_cast<const u32x4*>(x + t * d + c);
+}
+
+// Fused gather-sum: the shared down GEMM writes out[t] = sum_i w y + shared.
+struct FuseCombine {
+  void* out;
+  const void* y_sorted;
+  const float* topk_w;
+  const int32_t* inv_perm;
+};
+
 template <typename T>
 void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const void* gu,
-                const void* dn, void* h_sorted, void* y_sorted, void* sa, void* sb,
+                const void* dn, void* h_sorted, void* y_sorted, void* sa, void* sb, void* x_sorted,
                 hipStream_t s) {
   const int64_t S = p.tokens * p.top_k;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
+  if (x_sorted)
+    MOE_LAUNCH("sort_rows", sort_rows_kernel<T>, dim3(static_cast<unsigned>((S + 3) / 4)), dim3(256),
+               0, s, static_cast<const T*>(x), r.perm, p.top_k, S, p.d_model,
+               static_cast<T*>(x_sorted));
   GemmArgs a{};
-  a.a = x;
+  a.a = x_sorted ? x_sorted : x;
   a.lda = p.d_model;
   a.perm = r.perm;
   a.topk = p.top_k;
@@ -98,7 +125,8 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   a.sa = sa;
   a.sb = sb;
   a.lds = 2 * static_cast<int64_t>(p.d_hidden);
-  grouped_gemm<T, true, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
+  if (x_sorted) grouped_gemm<T, false, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
+  else grouped_gemm<T, true, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
 
   GemmArgs b{};
   b.a = h_sorted;
@@ -116,7 +144,7 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
 
 template <typename T>
 void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void* sdn, void* hs,
-                void* out, void* sa, void* sb, hipStream_t s) {
+                void* out, void* sa, void* sb, const FuseCombine* fuse, hipStream_t s) {
   GemmArgs a{};
   a.a = x;
   a.lda = p.d_model;
@@ -140,13 +168,22 @@ void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void
   b.M = p.tokens;
   b.c = out;
   b.ldc = p.d_model;
-  dense_gemm<T, kEpiStore>("shared_down", b, s);
+  if (fuse) {
+    b.c = fuse->out;
+    b.gy = fuse->y_sorted;
+    b.gw = fuse->topk_w;
+    b.ginv = fuse->inv_perm;
+    b.gk = p.top_k;
+    dense_gemm<T, kEpiCombine>("shared_down_combine", b, s);
+  } else {
+    dense_gemm<T, kEpiStore>("shared_down", b, s);
+  }
 }
 
 template <typename T>
 hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
                      const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
-                     void* ws, hipStream_t s) {
+                     void* ws, void* x_sorted, const FuseCombine* fuse, hipStream_t s) {
   const FfnLayout L = ffn_layout(p, saved != nullptr);
   char* W = static_cast<char*>(ws);
   char* SV = static_cast<char*>(saved);
@@ -160,12 +197,12 @@ hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
   T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
-  routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, s);
+  routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, x_sorted, s);
   if (hs > 0) {
     T* hsb = saved ? reinterpret_cast<T*>(SV + L.sv_sh) : reinterpret_cast<T*>(W + L.h_shared);
     T* ssa = saved ? reinterpret_cast<T*>(SV + L.sv_sab) : nullptr;
     T* ssb = saved ? ssa + hs : nullptr;
-    shared_ffn<T>(p, x, W + L.sgu_packed, W + L.sdown_packed, hsb, shared_out, ssa, ssb, s);
+    shared_ffn<T>(p, x, W + L.sgu_packed, W + L.sdown_packed, hsb, shared_out, ssa, ssb, fuse, s);
   }
   return hipGetLastError();
 }
@@ -197,8 +234,48 @@ FfnLayout ffn_layout(const moe_problem& p, bool training) {
 hipError_t launch_ffn_fwd(const moe_problem& p, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
                           void* ws, hipStream_t s) {
-  if (p.dtype == MOE_BF16) return ffn_fwd_t<bf16_t>(p, x, w, r, y_sorted, shared_out, saved, ws, s);
-  return ffn_fwd_t<float>(p, x, w, r, y_sorted, shared_out, saved, ws, s);
+  if (p.dtype == MOE_BF16)
+    return ffn_fwd_t<bf16_t>(p, x, w, r, y_sorted, shared_out, saved, ws, nullptr, nullptr, s);
+  return ffn_fwd_t<float>(p, x, w, r, y_sorted, shared_out, saved, ws, nullptr, nullptr, s);
+}
+
+ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training) {
+  const size_t es = p.dtype == MOE_BF16 ? 2 : 4;
+  const size_t T = static_cast<size_t>(p.tokens), S = T * p.top_k;
+  ForwardLayout L{};
+  L.fused = dispatch == MOE_DISPATCH_FUSED_GSUM && p.d_shared > 0 && p.top_k <= kCombineMaxK;
+  size_t o = permute_ws_bytes(static_cast<int64_t>(S), p.experts);
+  const size_t f = ffn_layout(p, training).total;
+  o = align_up(o > f ? o : f, 256);
+  L.shared_out = o;
+  if (p.d_shared > 0 && !L.fused) o = align_up(o + T * p.d_model * es, 256);
+  L.x_sorted = o;
+  if (dispatch == MOE_DISPATCH_SORTED) o = align_up(o + S * p.d_model * es, 256);
+  L.total = o > 256 ? o : 256;
+  return L;
+}
+
+hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, const moe_weights& w,
+                          const moe_routing& r, void* y_sorted, void* saved, void* out, void* ws,
+                          hipStream_t s) {
+  const ForwardLayout L = forward_layout(p, dispatch, saved != nullptr);
+  char* W = static_cast<char*>(ws);
+  hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
+                              r.topk_idx, r.topk_w, s);
+  if (e != hipSuccess) return e;
+  e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, r.topk_idx, r.expert_offsets, r.perm,
+                     r.inv_perm, r.tiles, r.num_tiles, ws, s);
+  if (e != hipSuccess) return e;
+  void* shared_out = p.d_shared > 0 && !L.fused ? W + L.shared_out : nullptr;
+  void* x_sorted = dispatch == MOE_DISPATCH_SORTED ? W + L.x_sorted : nullptr;
+  const FuseCombine fuse{out, y_sorted, r.topk_w, r.inv_perm};
+  const FuseCombine* fp = L.fused ? &fuse : nullptr;
+  e = p.dtype == MOE_BF16
+          ? ffn_fwd_t<bf16_t>(p, x, w, r, y_sorted, shared_out, saved, ws, x_sorted, fp, s)
+          : ffn_fwd_t<float>(p, x, w, r, y_sorted, shared_out, saved, ws, x_sorted, fp, s);
+  if (e != hipSuccess || L.fused) return e;
+  return launch_combine(p.dtype, p.tokens, p.top_k, p.d_model, y_sorted, r.topk_w, r.inv_perm,
+                        shared_out, out, s);
 }
 
 }  // namespace moe

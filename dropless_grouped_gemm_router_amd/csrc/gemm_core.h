@@ -27,9 +27,14 @@ namespace moe {
 enum EpiMode {
   kEpiStore = 0,     // c[row][n] = acc
   kEpiSwiglu = 1,    // packed gate|up columns -> c[row][j] = SiLU(gate) * up (+ saved gate, up)
-  kEpiSwigluBwd = 2  // acc = dH[row][j]; with saved gate a and up b:
+  kEpiSwigluBwd = 2, // acc = dH[row][j]; with saved gate a and up b:
                      // c[row][j] = dH b SiLU'(a), c[row][h + j] = dH SiLU(a)
+  kEpiCombine = 3    // dense rows are tokens t: v = acc rounded to the storage type,
+                     // c[t][n] = sum_i gw[t,i] * gy[ginv[t*gk + i]][n] + v
 };
+
+// Largest top_k the fused gather-sum epilogue takes.
+constexpr int kCombineMaxK = 8;
 
 struct GemmArgs {
   const void* a;          // token-side rows
@@ -52,7 +57,40 @@ struct GemmArgs {
   void* sb;                 // SwiGLU: saved up pre-activations
   int64_t lds;              // row stride of sa / sb
   int hsplit;               // SwiGLU backward: column offset of the up gradient in c
+  const void* gy;           // fused combine: expert-sorted rows, row stride ldc
+  const float* gw;          // fused combine: [M][gk] weights
+  const int32_t* ginv;      // fused combine: [M][gk] sorted row of each (token, rank)
+  int gk;                   // fused combine: top_k (<= kCombineMaxK)
 };
+
+// Value of v once stored in T and read back.
+__device__ __forceinline__ float round_to(float v, const bf16_t*) { return bf16_to_f32(f32_to_bf16(v)); }
+__device__ __forceinline__ float round_to(float v, const float*) { return v; }
+
+// Fused gather-sum for four consecutive columns n.. of token t, in the
+// combine stage's order: fp32 multiply-adds over ranks 0..k-1 from zero,
+// then the (already rounded) dense value v added. idx and wt hold the
+// token's sorted rows and weights.
+template <typename T>
+__device__ __forceinline__ void combine4(const GemmArgs& p, int64_t t, int n, const float (&v)[4],
+                                         const int (&idx)[kCombineMaxK],
+                                         const float (&wt)[kCombineMaxK]) {
+  const T* y = static_cast<const T*>(p.gy);
+  float yv[kCombineMaxK][4];
+#pragma unroll
+  for (int i = 0; i < kCombineMaxK; ++i)
+    if (i < p.gk) load4(y + static_cast<int64_t>(idx[i]) * p.ldc + n, yv[i]);
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < kCombineMaxK; ++i)
+    if (i < p.gk) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(wt[i], yv[i][q], acc[q]);
+    }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] += v[q];
+  store4(static_cast<T*>(p.c) + t * p.ldc + n, acc[0], acc[1], acc[2], acc[3]);
+}
 
 template <int BM_, int WAVES_M_, int WAVES_N_, int WM_SUB_, int WN_SUB_, int PF_ = 2>
 struct TileCfg {
@@ -173,10 +211,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p,
     const int m = wm * WM_SUB * 32 + i * 32 + r32;
     if (m >= rows) continue;
     const int64_t orow = static_cast<int64_t>(row0) + m;
+    int idx[kCombineMaxK];
+    float wt[kCombineMaxK];
+    if (kEpi == kEpiCombine) {
+#pragma unroll
+      for (int ii = 0; ii < kCombineMaxK; ++ii) {
+        idx[ii] = ii < p.gk ? p.ginv[orow * p.gk + ii] : 0;
+        wt[ii] = ii < p.gk ? p.gw[orow * p.gk + ii] : 0.0f;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < WN_SUB; ++j) {
       const int n0 = nt * BN + wn * WN_SUB * 32 + j * 32;
-      if (kEpi == kEpiStore) {
+      if (kEpi == kEpiCombine) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float v[4] = {round_to(acc[i][j][4 * rr + 0], c), round_to(acc[i][j][4 * rr + 1], c),
+                              round_to(acc[i][j][4 * rr + 2], c), round_to(acc[i][j][4 * rr + 3], c)};
+          combine4<T>(p, orow, n0 + 8 * rr + 4 * g, v, idx, wt);
+        }
+      } else if (kEpi == kEpiStore) {
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int n = n0 + 8 * rr + 4 * g;

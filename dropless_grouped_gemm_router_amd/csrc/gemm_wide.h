@@ -169,6 +169,54 @@ __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int6
   }
 }
 
+// Fused gather-sum drain (kEpiCombine, dense rows = tokens): region row r
+// holds token orow + r's dense results, already rounded to bf16; the
+// wave's comb area holds each row's sorted rows ([64][k] int32) and weights
+// ([64][k] fp32 at byte 2048). Each 16-byte output piece is the combine
+// stage's sum, in its order: fp32 multiply-adds over ranks 0..k-1 from zero,
+// then the dense value. All k row loads of a piece are issued before use.
+__device__ __forceinline__ void wide_drain_combine(const GemmArgs& p, const char* region,
+                                                   const char* comb, int64_t orow, int col,
+                                                   int rows, int lane) {
+  const bf16_t* y = static_cast<const bf16_t*>(p.gy);
+  bf16_t* out = static_cast<bf16_t*>(p.c);
+  const int32_t* cidx = reinterpret_cast<const int32_t*>(comb);
+  const float* cw = reinterpret_cast<const float*>(comb + 2048);
+  const int K = p.gk;
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k) {
+    const int r = k * 8 + (lane >> 3), c = lane & 7;
+    if (r >= rows) break;
+    const u32x4 sv = *reinterpret_cast<const u32x4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+    int idx[kCombineMaxK];
+    float wt[kCombineMaxK];
+#pragma unroll
+    for (int i = 0; i < kCombineMaxK; ++i) {
+      idx[i] = i < K ? cidx[r * K + i] : 0;
+      wt[i] = i < K ? cw[r * K + i] : 0.0f;
+    }
+    u32x4 yv[kCombineMaxK];
+#pragma unroll
+    for (int i = 0; i < kCombineMaxK; ++i)
+      if (i < K) yv[i] = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(idx[i]) * p.ldc + col + c * 8);
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int i = 0; i < kCombineMaxK; ++i)
+      if (i < K) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] = __builtin_fmaf(wt[i], bf16lo(yv[i][q]), acc[2 * q]);
+          acc[2 * q + 1] = __builtin_fmaf(wt[i], bf16hi(yv[i][q]), acc[2 * q + 1]);
+        }
+      }
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(acc[2 * q] + bf16lo(sv[q]), acc[2 * q + 1] + bf16hi(sv[q]));
+    *reinterpret_cast<u32x4*>(out + (orow + r) * p.ldc + col + c * 8) = o;
+  }
+}
+
 // Parks the wave's 64 x 64 block of SwiGLU results (kWhich 0), gate
 // pre-activations (1) or up pre-activations (2). Packed columns j*32 +
 // [0,16) are gate columns and j*32 + [16,32) the matching up columns, so
@@ -193,18 +241,45 @@ __device__ __forceinline__ void wide_park_swiglu(
       }
 }
 
-// Wave epilogue of one wide tile for the plain store and the forward SwiGLU.
+// Wave epilogue of one wide tile for the plain store, the forward SwiGLU and
+// the fused gather-sum (comb: the wave's 4 KiB index area, else unused).
 // Accumulator register q of MFMA tile (i, j) holds row i*32 + r32 and
 // column j*32 + 8*(q/4) + 4*g + q%4 of the wave's 64 x 128 block.
 template <int kEpi>
 __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
                                               const f32x16_t (&acc)[WideCfg::WM_SUB][WideCfg::WN_SUB],
-                                              char* region, int row0, int rows, int nt, int wm,
-                                              int wn, int g, int r32, int lane) {
+                                              char* region, char* comb, int row0, int rows,
+                                              int nt, int wm, int wn, int g, int r32, int lane) {
   const int wrows = rows - wm * 64;  // rows of this wave's block that exist
   const int64_t orow = static_cast<int64_t>(row0) + wm * 64;
   bf16_t* c = static_cast<bf16_t*>(p.c);
-  if (kEpi == kEpiStore) {
+  if (kEpi == kEpiCombine) {
+    // The block's 64 tokens own 64 k consecutive entries of ginv and gw.
+    const int K = p.gk;
+    const int valid = (wrows < 64 ? (wrows > 0 ? wrows : 0) : 64) * K;
+#pragma unroll
+    for (int j = 0; j < kCombineMaxK; ++j) {
+      const int e = lane + 64 * j;
+      if (j < K && e < valid) {
+        reinterpret_cast<int32_t*>(comb)[e] = p.ginv[orow * K + e];
+        reinterpret_cast<float*>(comb + 2048)[e] = p.gw[orow * K + e];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const f32x16_t& a = acc[i][2 * h + jj];
+            wide_park(region, i * 32 + r32, jj * 64 + rr * 16 + g * 8, a[4 * rr], a[4 * rr + 1],
+                      a[4 * rr + 2], a[4 * rr + 3]);
+          }
+      wide_drain_combine(p, region, comb, orow, nt * WideCfg::BN + wn * 128 + h * 64, wrows, lane);
+    }
+  } else if (kEpi == kEpiStore) {
     // Two passes of 64 columns (MFMA tiles j = 2h, 2h + 1).
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -263,7 +338,9 @@ template <bool kGather, int kEpi, bool kDense>
 __global__ __launch_bounds__(WideCfg::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
                       const int32_t* __restrict__ num_tiles, int total_work) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kWideStage];
+  // The fused gather-sum epilogue adds 4 KiB per wave for its rows' indices
+  // and weights (160 KiB in all, the CU's LDS).
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kWideStage + (kEpi == kEpiCombine ? 8 * 4096 : 0)];
   const int n_tiles_n = p.N / WideCfg::BN;
   const int G = gridDim.x;
   const int nx = G < 8 ? G : 8;
@@ -347,7 +424,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
       buf ^= 1;
     }
 
-    if (kEpi != kEpiStore) {
+    if (kEpi != kEpiStore && kEpi != kEpiCombine) {
       // SwiGLU outputs are half the tile (or read saved values): stored
       // straight from the accumulators.
       gemm_epilogue<bf16_t, WideCfg, kEpi>(p, acc, cur.row0, cur.rows, nt, wm, wn, g, r32);
@@ -355,8 +432,10 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
       // The buffer of the last stage is free once every wave is done with it
       // (the other one is receiving the next item's first stage).
       wide_barrier();
-      wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192, cur.row0,
-                          cur.rows, nt, wm, wn, g, r32, lane);
+      wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192,
+                          kEpi == kEpiCombine ? smem + 2 * kWideStage + wave * 4096 : nullptr,
+                          cur.row0, cur.rows, nt, wm, wn, g,
+                          r32, lane);
     }
 
     if (nxt.rows <= 0) break;

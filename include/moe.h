@@ -220,6 +220,52 @@ int moe_combine(const moe_problem* p, const void* y_sorted, const moe_routing* r
                 const void* shared_out, void* out, void* stream);
 
 /*
+ * Dispatch variants of the forward (kernel_gmm_gpu.json, "layer" suite
+ * records, field "dispatch"; the pages name the variants and time them but
+ * do not define them). All give the same out, y_sorted and saved buffers,
+ * bit for bit: they differ in where token rows are gathered and where the
+ * combine runs, not in any arithmetic.
+ *   GATHER     the gate/up GEMM reads token rows through perm (moe_ffn_fwd,
+ *              then moe_combine).
+ *   SORTED     token rows are first copied into expert order (x_sorted
+ *              [S, d_model] in the workspace) and the gate/up GEMM reads
+ *              that copy row by row.
+ *   FUSED_GSUM the gather-sum combine runs in the epilogue of the shared
+ *              expert's down GEMM, whose rows are tokens: each output row is
+ *              written once, and the shared output is never stored. Needs
+ *              d_shared > 0 and top_k <= 8; otherwise it runs as GATHER.
+ * The pages' fourth variant, "fused" (a scatter-add from the expert GEMM
+ * into out), needs floating-point atomics and is not offered.
+ */
+typedef enum {
+  MOE_DISPATCH_GATHER = 0,
+  MOE_DISPATCH_SORTED = 1,
+  MOE_DISPATCH_FUSED_GSUM = 2
+} moe_dispatch;
+
+/*
+ * Workspace bytes (host) of moe_forward for a dispatch variant, with
+ * training = 1 when saved activations are written. 0 for an invalid
+ * problem or dispatch.
+ */
+size_t moe_forward_workspace_bytes(const moe_problem* p, int dispatch, int training);
+
+/*
+ * The whole forward in one call: "route", "sort_permute",
+ * "experts_grouped_swiglu" and "unpermute_combine" (kernel_gmm_gpu.json
+ * "pieces" suite), enqueued in that order on `stream`, with the dispatch
+ * variant above. Writes every array of r (as moe_route and moe_permute
+ * do), y_sorted [S, d_model], out [tokens, d_model] and, when saved is not
+ * NULL, the moe_saved_bytes(p) activations moe_bwd reads. The shared
+ * expert's output lives in the workspace (or nowhere, FUSED_GSUM).
+ * workspace: >= moe_forward_workspace_bytes(p, dispatch, saved != NULL).
+ * MOE_ERR_INVALID for an unknown dispatch value.
+ */
+int moe_forward(const moe_problem* p, int dispatch, const void* x, const moe_weights* w,
+                moe_routing* r, void* y_sorted, void* saved, void* out, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/*
  * Train-step backward (gpu_moe_h100.json header: value and gradient with
  * respect to the parameters and the input) of L = sum(out * grad_out),
  * with the top-k selection held fixed and the gradient reaching w_router

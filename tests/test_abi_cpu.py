@@ -25,7 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -140,6 +140,53 @@ def test_ffn_and_combine_argument_errors():
            workspace_bytes=need, stream=0)
     expect(B.MOE_ERR_INVALID, B.moe_combine, P, y, dict(r, inv_perm=None), sh, out, stream=0)
     expect(B.MOE_ERR_INVALID, B.moe_combine, P, y, r, FakeTensor(0x51000004), out, stream=0)
+
+
+def test_forward_workspace_sizes():
+    es = 2
+    T, S, d = P.tokens, P.tokens * P.top_k, P.d_model
+    base = B.moe_workspace_bytes(P)
+    g = B.moe_forward_workspace_bytes(P, "gather")
+    s = B.moe_forward_workspace_bytes(P, "sorted")
+    f = B.moe_forward_workspace_bytes(P, "fused_gsum")
+    # gather stages the shared output after the permute/FFN area, sorted also
+    # the expert-ordered token copy, fused_gsum neither.
+    assert g >= base + T * d * es
+    assert s >= g + S * d * es
+    assert base <= f < g
+    # no shared expert or top_k > 8: fused_gsum needs what gather needs
+    p0 = Problem(100, 8, 2, 256, 128, 0, "bf16", 64)
+    assert B.moe_forward_workspace_bytes(p0, "fused_gsum") == B.moe_forward_workspace_bytes(p0, "gather")
+    p9 = Problem(100, 16, 9, 256, 128, 128, "bf16", 64)
+    assert B.moe_forward_workspace_bytes(p9, "fused_gsum") == B.moe_forward_workspace_bytes(p9, "gather")
+    # training keeps the hidden activations in the saved buffer instead
+    assert T * d * es < B.moe_forward_workspace_bytes(P, "gather", training=True) < g
+    assert B.moe_forward_workspace_bytes(P, 3) == 0
+    assert B.moe_forward_workspace_bytes(Problem(100, 8, 2, 500, 128, 0, "bf16", 64), 0) == 0
+
+
+def test_forward_argument_errors():
+    r, w = fake_routing(), fake_weights()
+    ws = FakeTensor(0x40000000)
+    y, out, x = FakeTensor(0x50000000), FakeTensor(0x52000000), FakeTensor(0x53000000)
+    for disp in ("gather", "sorted", "fused_gsum"):
+        need = B.moe_forward_workspace_bytes(P, disp)
+        expect(B.MOE_ERR_WORKSPACE, B.moe_forward, P, disp, x, w, r, y, None, out, ws,
+               workspace_bytes=need - 1, stream=0)
+        expect(B.MOE_ERR_INVALID, B.moe_forward, P, disp, x, w, dict(r, tiles=None), y, None, out,
+               ws, workspace_bytes=need, stream=0)
+        expect(B.MOE_ERR_INVALID, B.moe_forward, P, disp, x, w, r, y, None, None, ws,
+               workspace_bytes=need, stream=0)
+        expect(B.MOE_ERR_INVALID, B.moe_forward, P, disp, x, fake_weights(shared=False), r, y, None,
+               out, ws, workspace_bytes=need, stream=0)
+        expect(B.MOE_ERR_INVALID, B.moe_forward, P, disp, x, w, r, y, FakeTensor(0x60000010), out,
+               ws, workspace_bytes=need, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_forward, P, 3, x, w, r, y, None, out, ws,
+           workspace_bytes=1 << 40, stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_forward, P, -1, x, w, r, y, None, out, ws,
+           workspace_bytes=1 << 40, stream=0)
+    B.moe_forward(Problem(0, 8, 2, 256, 128, 0, "bf16", 64), "fused_gsum", None, {}, {}, None, None,
+                  None, None, workspace_bytes=0, stream=0)
 
 
 def test_bwd_argument_errors():
