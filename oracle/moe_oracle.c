@@ -28,6 +28,15 @@
  * except the router logits, which follow one fixed fp32 order (see
  * oracle_route) so that expert choices can be compared exactly.
  *
+ *
+ * Capacity routing (kernel_gmm_gpu.json records with "routing": "capacity";
+ * the pages give neither the capacity nor the drop rule, so this is the
+ * reading adopted): each expert takes at most `capacity` token-slots, the
+ * first ones in flat slot order t*k+i; a dropped slot contributes nothing
+ * to the output and no gradient to its expert's weights, the kept weights
+ * are not renormalised, and the router gradient still flows through every
+ * selected slot's weight. capacity 0 means dropless.
+ *
  * Parity pins (all in the CPU test suite): dense every-expert-masked brute
  * force, finite differences, closed-form special cases (all-zero router,
  * k == E, E == k == 1, identical experts, k == 1), the constructed
@@ -122,14 +131,15 @@ ORACLE_API int oracle_route(int64_t T, int d, int E, int k, const float* x, cons
  *   offsets[e]     = sum of counts[e'] for e' < e; offsets[E] = T*k
  *   perm[slot]     = flat slot t*k+i placed at sorted position slot, where the
  *                    slots of one expert keep ascending flat order
- *   inv_perm[flat] = its sorted position
+ *   inv_perm[flat] = its sorted position, or -1 when capacity > 0 and the
+ *                    slot is not among the first `capacity` of its expert
  *   tiles[3*n..]   = (expert, first sorted row, rows) for each block_m-row
- *                    piece of each expert, experts ascending
+ *                    piece of each expert's kept rows, experts ascending
  * Returns the number of tiles, or -1 on an out-of-range expert index.
  */
-ORACLE_API int64_t oracle_permute(int64_t T, int k, int E, int bm, const int32_t* topk_idx,
-                                  int32_t* counts, int32_t* offsets, int32_t* perm,
-                                  int32_t* inv_perm, int32_t* tiles) {
+ORACLE_API int64_t oracle_permute(int64_t T, int k, int E, int bm, int capacity,
+                                  const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                                  int32_t* perm, int32_t* inv_perm, int32_t* tiles) {
   const int64_t S = T * k;
   for (int e = 0; e < E; ++e) counts[e] = 0;
   for (int64_t s = 0; s < S; ++s) {
@@ -142,15 +152,17 @@ ORACLE_API int64_t oracle_permute(int64_t T, int k, int E, int bm, const int32_t
   int32_t* next = (int32_t*)calloc((size_t)E, sizeof(int32_t));
   for (int64_t s = 0; s < S; ++s) {
     int e = topk_idx[s];
-    int32_t pos = offsets[e] + next[e]++;
+    int32_t rank = next[e]++;
+    int32_t pos = offsets[e] + rank;
     perm[pos] = (int32_t)s;
-    inv_perm[s] = pos;
+    inv_perm[s] = (capacity > 0 && rank >= capacity) ? -1 : pos;
   }
   free(next);
   int64_t n = 0;
   for (int e = 0; e < E; ++e) {
-    for (int32_t r = 0; r < counts[e]; r += bm) {
-      int32_t rows = counts[e] - r < bm ? counts[e] - r : bm;
+    int32_t kept = (capacity > 0 && counts[e] > capacity) ? capacity : counts[e];
+    for (int32_t r = 0; r < kept; r += bm) {
+      int32_t rows = kept - r < bm ? kept - r : bm;
       if (tiles) {
         tiles[3 * n + 0] = e;
         tiles[3 * n + 1] = offsets[e] + r;
@@ -198,14 +210,15 @@ static void ffn_row(int d, int h, const float* xr, const float* wg, const float*
  * present when hs > 0. When y_slots is non-NULL, y_slots[r*k+i,:] receives
  * the unweighted expert output of selection i (the sorted expert outputs,
  * indexed by flat slot). Weights of expert e: wg + e*d*h, wu + e*d*h,
- * wd + e*h*d.
+ * wd + e*h*d. keep (T*k flags, NULL = all kept): a slot with keep == 0 was
+ * dropped by capacity routing and contributes nothing (its y_slots row is 0).
  */
 ORACLE_API int oracle_forward_rows(int64_t nrows, const int64_t* rows, int d, int E, int k, int h,
                                    int hs, const float* x, const float* wg, const float* wu,
                                    const float* wd, const float* wsg, const float* wsu,
                                    const float* wsd, const int32_t* topk_idx,
-                                   const double* topk_w, double* out, double* y_slots,
-                                   int nthreads) {
+                                   const double* topk_w, const uint8_t* keep, double* out,
+                                   double* y_slots, int nthreads) {
   (void)E;
   set_threads(nthreads);
   int hmax = h > hs ? h : hs;
@@ -224,6 +237,10 @@ ORACLE_API int oracle_forward_rows(int64_t nrows, const int64_t* rows, int d, in
       for (int i = 0; i < k; ++i) {
         int64_t e = topk_idx[t * k + i];
         double w = topk_w[t * k + i];
+        if (keep && !keep[t * k + i]) {
+          if (y_slots) memset(y_slots + (r * k + i) * d, 0, sizeof(double) * (size_t)d);
+          continue;
+        }
         ffn_row(d, h, xr, wg + e * d * h, wu + e * d * h, wd + e * h * d, a, b, g, y);
         for (int j = 0; j < d; ++j) o[j] += w * y[j];
         if (y_slots) memcpy(y_slots + (r * k + i) * d, y, sizeof(double) * (size_t)d);
@@ -274,6 +291,9 @@ static void ffn_row_bwd(int d, int h, const float* wg, const float* wu, const fl
  *   dl_i = w_i (dw_i - sum_j w_j dw_j) on the kept experts, 0 elsewhere
  *   dW_r += x_t^T dl;  dx_t += dl W_r^T
  *   shared expert: the same steps with weight 1.
+ * A slot dropped by capacity routing (keep[s] == 0; keep NULL = all kept)
+ * has y_i = 0: dw_i = 0, no expert-weight or expert-path input gradient,
+ * while dl_i = w_i (0 - sum_j w_j dw_j) still reaches the router.
  * All outputs are double and fully overwritten; the shared ones are touched
  * only when hs > 0. Weight gradients of expert e are reduced over tokens in
  * ascending token order.
@@ -282,8 +302,9 @@ ORACLE_API int oracle_backward(int64_t T, int d, int E, int k, int h, int hs, co
                                const float* wr, const float* wg, const float* wu, const float* wd,
                                const float* wsg, const float* wsu, const float* wsd,
                                const float* G, const int32_t* topk_idx, const double* topk_w,
-                               double* dx, double* dwr, double* dwg, double* dwu, double* dwd,
-                               double* dwsg, double* dwsu, double* dwsd, int nthreads) {
+                               const uint8_t* keep, double* dx, double* dwr, double* dwg,
+                               double* dwu, double* dwd, double* dwsg, double* dwsu, double* dwsd,
+                               int nthreads) {
   set_threads(nthreads);
   const int64_t S = T * k;
   /* Per-slot and per-token intermediates (phase 1, token-parallel). */
@@ -319,6 +340,10 @@ ORACLE_API int oracle_backward(int64_t T, int d, int E, int k, int h, int hs, co
         double w = topk_w[s];
         double* a = G_a + s * h;
         double* b = G_b + s * h;
+        if (keep && !keep[s]) {
+          dw[i] = 0.0;
+          continue;
+        }
         ffn_row(d, h, xr, wg + e * d * h, wu + e * d * h, wd + e * h * d, a, b, g, y);
         double acc = 0.0;
         for (int j = 0; j < d; ++j) {
@@ -376,7 +401,7 @@ ORACLE_API int oracle_backward(int64_t T, int d, int E, int k, int h, int hs, co
     for (int64_t t = 0; t < T; ++t) {
       for (int i = 0; i < k; ++i) {
         int64_t s = t * k + i;
-        if (topk_idx[s] != e) continue;
+        if (topk_idx[s] != e || (keep && !keep[s])) continue;
         const float* xr = x + t * d;
         const float* Gt = G + t * d;
         double w = topk_w[s];

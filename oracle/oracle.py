@@ -51,11 +51,11 @@ def _load():
         lib.oracle_route.restype = i32
         lib.oracle_route.argtypes = [i64, i32, i32, i32, P, P, P, P, P, i32]
         lib.oracle_permute.restype = i64
-        lib.oracle_permute.argtypes = [i64, i32, i32, i32, P, P, P, P, P, P]
+        lib.oracle_permute.argtypes = [i64, i32, i32, i32, i32, P, P, P, P, P, P]
         lib.oracle_forward_rows.restype = i32
-        lib.oracle_forward_rows.argtypes = [i64, P, i32, i32, i32, i32, i32] + [P] * 9 + [P, P, i32]
+        lib.oracle_forward_rows.argtypes = [i64, P, i32, i32, i32, i32, i32] + [P] * 10 + [P, P, i32]
         lib.oracle_backward.restype = i32
-        lib.oracle_backward.argtypes = [i64, i32, i32, i32, i32, i32] + [P] * 11 + [P] * 8 + [i32]
+        lib.oracle_backward.argtypes = [i64, i32, i32, i32, i32, i32] + [P] * 12 + [P] * 8 + [i32]
         _lib = lib
     return _lib
 
@@ -93,7 +93,9 @@ def max_tiles(T: int, k: int, E: int, bm: int) -> int:
     return (T * k + bm - 1) // bm + E
 
 
-def permute(topk_idx: np.ndarray, E: int, bm: int) -> Dict[str, np.ndarray]:
+def permute(topk_idx: np.ndarray, E: int, bm: int, capacity: int = 0) -> Dict[str, np.ndarray]:
+    """Stable grouping by expert and the tile list; with capacity > 0 each
+    expert keeps its first ``capacity`` slots (inv_perm -1 for the others)."""
     idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     T, k = idx.shape
     S = T * k
@@ -102,18 +104,28 @@ def permute(topk_idx: np.ndarray, E: int, bm: int) -> Dict[str, np.ndarray]:
     perm = np.empty(S, np.int32)
     inv = np.empty(S, np.int32)
     tiles = np.empty((max_tiles(T, k, E, bm), 3), np.int32)
-    n = _load().oracle_permute(T, k, E, bm, _p(idx), _p(counts), _p(offsets), _p(perm), _p(inv),
-                               _p(tiles))
+    n = _load().oracle_permute(T, k, E, bm, int(capacity), _p(idx), _p(counts), _p(offsets),
+                               _p(perm), _p(inv), _p(tiles))
     if n < 0:
         raise ValueError("expert index out of range")
     return dict(counts=counts, offsets=offsets, perm=perm, inv_perm=inv, tiles=tiles[:n].copy(),
                 num_tiles=int(n))
 
 
+def keep_mask(perm: Dict[str, np.ndarray], T: int, k: int) -> np.ndarray:
+    """[T, k] flags of the slots a capacity-routed permute kept."""
+    return (perm["inv_perm"] >= 0).reshape(T, k)
+
+
+def _keep(keep, T, k):
+    return None if keep is None else np.ascontiguousarray(np.asarray(keep).reshape(T, k), np.uint8)
+
+
 def forward_rows(x, w_gate, w_up, w_down, topk_idx, topk_w, ws_gate=None, ws_up=None,
                  ws_down=None, rows: Optional[Sequence[int]] = None, want_y: bool = False,
-                 nthreads: int = 0):
-    """Output rows (float64). ``rows`` selects tokens (default: all)."""
+                 nthreads: int = 0, keep=None):
+    """Output rows (float64). ``rows`` selects tokens (default: all);
+    ``keep`` ([T, k] flags) marks the slots capacity routing kept."""
     x = _f32(x)
     T, d = x.shape
     E, _, h = w_gate.shape
@@ -132,15 +144,17 @@ def forward_rows(x, w_gate, w_up, w_down, topk_idx, topk_w, ws_gate=None, ws_up=
         n = rows_arr.size
     out = np.empty((n, d), np.float64)
     y = np.empty((n * k, d), np.float64) if want_y else None
+    kp = _keep(keep, T, k)
     _load().oracle_forward_rows(n, _p(rows_arr), d, E, k, h, hs, _p(x), _p(wg), _p(wu), _p(wd),
-                                _p(wsg), _p(wsu), _p(wsd), _p(idx), _p(w), _p(out), _p(y),
+                                _p(wsg), _p(wsu), _p(wsd), _p(idx), _p(w), _p(kp), _p(out), _p(y),
                                 nthreads)
     return (out, y) if want_y else out
 
 
 def backward(x, w_router, w_gate, w_up, w_down, grad_out, topk_idx, topk_w, ws_gate=None,
-             ws_up=None, ws_down=None, nthreads: int = 0) -> Dict[str, np.ndarray]:
-    """Gradients of sum(out * grad_out) (float64), selection held fixed."""
+             ws_up=None, ws_down=None, nthreads: int = 0, keep=None) -> Dict[str, np.ndarray]:
+    """Gradients of sum(out * grad_out) (float64), selection (and, with
+    ``keep``, the capacity drops) held fixed."""
     x = _f32(x)
     T, d = x.shape
     E, _, h = w_gate.shape
@@ -160,7 +174,8 @@ def backward(x, w_router, w_gate, w_up, w_down, grad_out, topk_idx, topk_w, ws_g
         g.update(ws_gate=np.empty((d, hs)), ws_up=np.empty((d, hs)), ws_down=np.empty((hs, d)))
     _load().oracle_backward(
         T, d, E, k, h, hs, _p(x), _p(wr), _p(wg), _p(wu), _p(wd), _p(wsg), _p(wsu), _p(wsd), _p(G),
-        _p(idx), _p(w), _p(g["x"]), _p(g["w_router"]), _p(g["w_gate"]), _p(g["w_up"]),
+        _p(idx), _p(w), _p(_keep(keep, T, k)), _p(g["x"]), _p(g["w_router"]), _p(g["w_gate"]),
+        _p(g["w_up"]),
         _p(g["w_down"]), _p(g.get("ws_gate")), _p(g.get("ws_up")), _p(g.get("ws_down")), nthreads)
     return g
 

@@ -57,11 +57,16 @@ def bf_ffn(x, wg, wu, wd):
     return ((a * expit(a)) * b) @ wd
 
 
-def bf_forward(x, wr, wg, wu, wd, sel, ws=None, logits64=None):
+def bf_forward(x, wr, wg, wu, wd, sel, ws=None, logits64=None, keep=None):
     x = x.astype(np.float64)
     if logits64 is None:
         logits64 = x @ wr.astype(np.float64)
     W = bf_mask_weights(logits64, sel)
+    if keep is not None:
+        # capacity routing: a dropped slot's expert contributes nothing, the
+        # kept weights stay as they are
+        for t, i in zip(*np.nonzero(~keep)):
+            W[t, sel[t, i]] = 0.0
     out = np.zeros((x.shape[0], wd.shape[2]))
     for e in range(wg.shape[0]):
         out += W[:, e:e + 1] * bf_ffn(x, wg[e].astype(np.float64), wu[e].astype(np.float64),
@@ -301,25 +306,126 @@ def test_permute_rejects_bad_index():
         oracle.permute(np.array([[0, 5]], np.int32), 4, 32)
 
 
+# ------------------------------------------------------ capacity routing
+# kernel_gmm_gpu.json records with "routing": "capacity" (the pages define
+# neither the capacity nor the drop rule): an expert keeps its first C slots
+# in flat slot order t*k + i.
+
+def bf_keep(sel, E, C):
+    """Independent drop rule: a slot's position within its expert is the
+    running count of that expert over the flat slots up to it (cumulative
+    one-hot sums); capacity C keeps positions < C (C = 0: every slot)."""
+    T, k = sel.shape
+    flat = sel.reshape(-1)
+    onehot = np.zeros((T * k, E), np.int64)
+    onehot[np.arange(T * k), flat] = 1
+    pos = np.cumsum(onehot, axis=0)[np.arange(T * k), flat] - 1
+    return (pos < C).reshape(T, k) if C > 0 else np.ones((T, k), bool)
+
+
+@pytest.mark.parametrize("T,E,k,bm,C", [(67, 8, 2, 4, 9), (300, 64, 8, 32, 30), (129, 7, 3, 64, 1),
+                                        (50, 4, 2, 8, 25), (40, 5, 5, 16, 13)])
+def test_capacity_permute_matches_cumulative_count(T, E, k, bm, C):
+    rng = np.random.default_rng(T + C)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    full = oracle.permute(idx, E, bm)
+    r = oracle.permute(idx, E, bm, capacity=C)
+    keep = oracle.keep_mask(r, T, k)
+    assert np.array_equal(keep, bf_keep(idx, E, C))
+    # the sorted order is the dropless one; dropped slots lose their row
+    assert np.array_equal(r["perm"], full["perm"]) and np.array_equal(r["offsets"], full["offsets"])
+    flat_keep = keep.reshape(-1)
+    assert np.array_equal(r["inv_perm"][flat_keep], full["inv_perm"][flat_keep])
+    assert np.all(r["inv_perm"][~flat_keep] == -1)
+    # tiles cover exactly each expert's first min(count, C) rows, in block_m pieces
+    kept = np.minimum(r["counts"], C)
+    assert kept.sum() == flat_keep.sum()
+    expect = [(e, r["offsets"][e] + q, min(bm, kept[e] - q)) for e in range(E)
+              for q in range(0, kept[e], bm)]
+    assert r["num_tiles"] == len(expect)
+    assert np.array_equal(r["tiles"], np.array(expect, np.int32).reshape(-1, 3))
+
+
+def test_capacity_at_least_the_largest_load_is_dropless():
+    _, v = tiny_problem(40, 8, 2, 12, 6, 4, "bf16", seed=9)
+    _, idx, w = oracle.route(v["x"], v["w_router"], 2)
+    full = oracle.permute(idx, 8, 4)
+    C = int(full["counts"].max())
+    r = oracle.permute(idx, 8, 4, capacity=C)
+    for n in ("perm", "inv_perm", "offsets", "tiles"):
+        assert np.array_equal(r[n], full[n])
+    keep = oracle.keep_mask(r, 40, 2)
+    assert keep.all()
+    a = oracle.forward_rows(v["x"], v["w_gate"], v["w_up"], v["w_down"], idx, w, *shared_of(v), keep=keep)
+    b = oracle.forward_rows(v["x"], v["w_gate"], v["w_up"], v["w_down"], idx, w, *shared_of(v))
+    assert np.array_equal(a, b)
+    r1 = oracle.permute(idx, 8, 4, capacity=C - 1)
+    assert not oracle.keep_mask(r1, 40, 2).all()
+
+
+@pytest.mark.parametrize("T,E,k,d,h,hs,dtype,C", [(33, 4, 2, 16, 8, 0, "bf16", 10),
+                                                  (67, 8, 2, 16, 6, 5, "fp32", 12),
+                                                  (40, 8, 4, 12, 8, 0, "bf16", 15),
+                                                  (19, 64, 8, 32, 4, 6, "bf16", 2)])
+def test_capacity_forward_matches_dense_brute_force(T, E, k, d, h, hs, dtype, C):
+    _, v = tiny_problem(T, E, k, d, h, hs, dtype, seed=13)
+    logits, idx, w = oracle.route(v["x"], v["w_router"], k)
+    sel = bf_select(logits.astype(np.float64), k)
+    keep = bf_keep(sel, E, C)
+    assert not keep.all()
+    out, y = oracle.forward_rows(v["x"], v["w_gate"], v["w_up"], v["w_down"], idx, w,
+                                 *(shared_of(v) or (None, None, None)), want_y=True, keep=keep)
+    ref = bf_forward(v["x"], v["w_router"], v["w_gate"], v["w_up"], v["w_down"], sel, shared_of(v),
+                     logits64=logits.astype(np.float64), keep=keep)
+    assert oracle.rel_err(out, ref) < 1e-12
+    assert np.all(y[~keep.reshape(-1)] == 0.0)
+
+
+def test_capacity_zero_router_closed_form():
+    """All-zero router: every token picks experts 0..k-1 with weight 1/k, so
+    with capacity C exactly tokens 0..C-1 reach the experts and the rest get
+    the shared expert alone."""
+    T, E, k, C = 10, 4, 2, 6
+    _, v = tiny_problem(T, E, k, 8, 5, 3, "fp32", seed=2)
+    wr = np.zeros_like(v["w_router"])
+    _, idx, w = oracle.route(v["x"], wr, k)
+    r = oracle.permute(idx, E, 4, capacity=C)
+    keep = oracle.keep_mask(r, T, k)
+    assert keep[:C].all() and not keep[C:].any()
+    out = oracle.forward_rows(v["x"], v["w_gate"], v["w_up"], v["w_down"], idx, w, *shared_of(v),
+                              keep=keep)
+    x = v["x"].astype(np.float64)
+    sh = bf_ffn(x, *[a.astype(np.float64) for a in shared_of(v)])
+    ex = sum(bf_ffn(x, v["w_gate"][e].astype(np.float64), v["w_up"][e].astype(np.float64),
+                    v["w_down"][e].astype(np.float64)) for e in range(k)) / k
+    ref = sh.copy()
+    ref[:C] += ex[:C]
+    assert oracle.rel_err(out, ref) < 1e-12
+
+
 # ------------------------------------------------------ finite differences
 
-def fd_loss(v, sel, hs):
-    """L = sum(out * G) through the dense brute force, selection frozen,
-    logits in double."""
+def fd_loss(v, sel, hs, keep=None):
+    """L = sum(out * G) through the dense brute force, selection (and any
+    capacity drops) frozen, logits in double."""
     out = bf_forward(v["x"], v["w_router"], v["w_gate"], v["w_up"], v["w_down"], sel,
-                     shared_of(v) if hs else None)
+                     shared_of(v) if hs else None, keep=keep)
     return float(np.sum(out * v["grad_out"].astype(np.float64)))
 
 
-@pytest.mark.parametrize("T,E,k,d,h,hs", [(3, 2, 1, 4, 3, 0), (4, 3, 2, 5, 4, 2), (5, 4, 2, 8, 6, 3),
-                                          (2, 4, 4, 6, 2, 0)])
-def test_gradients_match_central_differences(T, E, k, d, h, hs):
+@pytest.mark.parametrize("T,E,k,d,h,hs,C", [(3, 2, 1, 4, 3, 0, 0), (4, 3, 2, 5, 4, 2, 0),
+                                            (5, 4, 2, 8, 6, 3, 0), (2, 4, 4, 6, 2, 0, 0),
+                                            (6, 3, 2, 5, 4, 2, 3), (5, 2, 2, 4, 3, 0, 3)])
+def test_gradients_match_central_differences(T, E, k, d, h, hs, C):
     _, v = tiny_problem(T, E, k, d, h, hs, "fp32", seed=21)
     v = {n: a.astype(np.float64) for n, a in v.items()}
     logits, idx, w = oracle.route(v["x"].astype(np.float32), v["w_router"].astype(np.float32), k)
     sel = idx.astype(np.int64)
+    keep = bf_keep(sel, E, C) if C else None
+    if C:
+        assert not keep.all()
     g = oracle.backward(v["x"], v["w_router"], v["w_gate"], v["w_up"], v["w_down"], v["grad_out"],
-                        idx, w, *(shared_of(v) if hs else (None, None, None)))
+                        idx, w, *(shared_of(v) if hs else (None, None, None)), keep=keep)
     eps = 1e-6
     names = ["x", "w_router", "w_gate", "w_up", "w_down"] + (["ws_gate", "ws_up", "ws_down"] if hs else [])
     for n in names:
@@ -330,9 +436,9 @@ def test_gradients_match_central_differences(T, E, k, d, h, hs):
             mi = it.multi_index
             old = base[mi]
             base[mi] = old + eps
-            lp = fd_loss(v, sel, hs)
+            lp = fd_loss(v, sel, hs, keep)
             base[mi] = old - eps
-            lm = fd_loss(v, sel, hs)
+            lm = fd_loss(v, sel, hs, keep)
             base[mi] = old
             fd[mi] = (lp - lm) / (2 * eps)
         # the oracle's weights come from fp32 logits, the brute force from double ones
