@@ -163,9 +163,10 @@ def cpu_baseline(p, inputs, sample_tokens):
     nthreads = oracle.max_threads()
     t0 = time.perf_counter()
     _, idx, w = oracle.route(x, v["w_router"], p.top_k, nthreads)
-    oracle.permute(idx, p.experts, p.block_m)
+    r = oracle.permute(idx, p.experts, p.block_m, capacity=p.capacity)
+    keep = oracle.keep_mask(r, sample_tokens, p.top_k) if p.capacity else None
     oracle.forward_rows(x, v["w_gate"], v["w_up"], v["w_down"], idx, w, v.get("ws_gate"),
-                        v.get("ws_up"), v.get("ws_down"), nthreads=nthreads)
+                        v.get("ws_up"), v.get("ws_down"), nthreads=nthreads, keep=keep)
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"first {sample_tokens} of the {p.tokens} tokens of the same seeded inputs: "
@@ -192,7 +193,7 @@ def train_step_line(B, steps, warmup):
     """Forward + backward on the train-step workload (16384 tokens)."""
     import torch
 
-    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, make_inputs
+    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, capacity_for, make_inputs
 
     name, p, _ = WORKLOADS[4]
     dev = B.device_inputs(make_inputs(p, seed=0, with_grad_out=True), "cuda:0")
@@ -220,6 +221,9 @@ def main():
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--dispatch", choices=["gather", "sorted", "fused_gsum"], default="gather",
                     help="forward dispatch variant (moe_forward)")
+    ap.add_argument("--capacity-factor", type=float, default=0.0,
+                    help="capacity routing: per-expert capacity ceil(F * tokens * top_k / "
+                         "experts); 0 = dropless")
     ap.add_argument("--skew", type=float, default=0.0,
                     help="routing skew of the synthetic router (inputs.Problem.skew)")
     ap.add_argument("--cpu-sample", type=int, default=131072,
@@ -256,13 +260,15 @@ def main():
     import torch
 
     from dropless_grouped_gemm_router_amd import binding as B
-    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, make_inputs
+    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, capacity_for, make_inputs
 
     name, p, _ = WORKLOADS[args.workload]
     if args.block_m:
         p = dataclasses.replace(p, block_m=args.block_m)
     if args.skew:
         p = dataclasses.replace(p, skew=args.skew)
+    if args.capacity_factor:
+        p = dataclasses.replace(p, capacity=capacity_for(p, args.capacity_factor))
     torch.cuda.set_device(0)
     print(f"bench: {name} bm={p.block_m}: generating inputs", file=sys.stderr, flush=True)
     inputs = make_inputs(p, seed=0)
@@ -321,7 +327,8 @@ def main():
                  + ("unskewed random router" if not p.skew else f"router skew {p.skew}")),
         "config": {"workload": name, "tokens": p.tokens, "experts": p.experts, "top_k": p.top_k,
                    "d_model": p.d_model, "d_hidden": p.d_hidden, "d_shared": p.d_shared,
-                   "block_m": p.block_m, "skew": p.skew, "dispatch": args.dispatch},
+                   "block_m": p.block_m, "skew": p.skew, "dispatch": args.dispatch,
+                   "routing": "capacity" if p.capacity else "dropless", "capacity": p.capacity},
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
         "roofline": roof,

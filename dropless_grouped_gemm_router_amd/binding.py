@@ -35,7 +35,7 @@ class moe_problem(ctypes.Structure):
     _fields_ = [("tokens", ctypes.c_int64), ("experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("d_model", ctypes.c_int32), ("d_hidden", ctypes.c_int32),
                 ("d_shared", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("block_m", ctypes.c_int32)]
+                ("block_m", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 class moe_weights(ctypes.Structure):
@@ -125,7 +125,7 @@ def problem_struct(p) -> moe_problem:
     return moe_problem(int(p.tokens), int(p.experts), int(p.top_k), int(p.d_model),
                        int(p.d_hidden), int(p.d_shared),
                        DTYPES[p.dtype] if isinstance(p.dtype, str) else int(p.dtype),
-                       int(p.block_m))
+                       int(p.block_m), int(getattr(p, "capacity", 0)))
 
 
 def _check(status: int, where: str):

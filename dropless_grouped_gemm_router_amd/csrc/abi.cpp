@@ -22,7 +22,7 @@ bool ok_ptr(const void* ptr, size_t a = 16) { return ptr != nullptr && aligned(p
 int check(const moe_problem* p) {
   if (!p) return MOE_ERR_INVALID;
   if (p->tokens < 0 || p->experts < 1 || p->top_k < 1 || p->top_k > p->experts ||
-      p->d_model < 1 || p->d_hidden < 1 || p->d_shared < 0)
+      p->d_model < 1 || p->d_hidden < 1 || p->d_shared < 0 || p->capacity < 0)
     return MOE_ERR_INVALID;
   if (p->dtype != MOE_FP32 && p->dtype != MOE_BF16) return MOE_ERR_INVALID;
   if (p->block_m != 32 && p->block_m != 64 && p->block_m != 128 && p->block_m != 256)
@@ -104,7 +104,8 @@ MOE_EXPORT int moe_permute(const moe_problem* p, moe_routing* r, void* workspace
     return MOE_ERR_INVALID;
   if (workspace_bytes < moe::permute_ws_bytes(p->tokens * p->top_k, p->experts))
     return MOE_ERR_WORKSPACE;
-  return hip_status(moe::launch_permute(p->tokens, p->top_k, p->experts, p->block_m, r->topk_idx,
+  return hip_status(moe::launch_permute(p->tokens, p->top_k, p->experts, p->block_m,
+                                        p->capacity, r->topk_idx,
                                         r->expert_offsets, r->perm, r->inv_perm, r->tiles,
                                         r->num_tiles, workspace, as_stream(stream)));
 }

@@ -56,7 +56,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // One wave per token: dY rows, dw by wave reduction, then dl for the kept
-// experts (lane i holds rank i; k <= 64).
+// experts (lane i holds rank i; k <= 64). A slot dropped by capacity
+// routing (inv_perm -1) has y = 0: dw = 0 and no dY row, while its dl
+// still carries the normalisation term.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     int64_t ntok, int k, int d, const T* __restrict__ G, const T* __restrict__ y,
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     const int64_t slot = inv_perm[t * k + i];
     const float wi = w[t * k + i];
     float dot = 0.0f;
-    for (int c = lane * N; c < d; c += 64 * N) {
+    for (int c = lane * N; slot >= 0 && c < d; c += 64 * N) {
       float g[N], yv[N], o[N];
       V16<T>::load(G + t * d + c, g);
       V16<T>::load(y + slot * d + c, yv);
@@ -92,18 +94,40 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
   if (lane < k) dl[t * k + lane] = my_w * (my_dw - s);
 }
 
-// Router weight gradient, stage 1: per tile of sorted rows (one expert),
-// partial[tile][j] = sum over the tile's rows, in order, of x[tok][j] * dl[slot].
+// Router weight gradient, stage 1: per block_m piece of an expert's sorted
+// rows, partial[piece][j] = sum over the piece's rows, in order, of
+// x[tok][j] * dl[slot]. The pieces are those of the dropless tile list
+// (experts ascending, block_m rows each, the last partial), derived from
+// the expert offsets: under capacity routing the dropped slots still carry
+// router gradient, though no GEMM tile covers their rows.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void router_partial_kernel(
     const T* __restrict__ x, int d, int topk, const int32_t* __restrict__ perm,
-    const float* __restrict__ dl, const int32_t* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, float* __restrict__ partial) {
-  __shared__ int64_t tok[256];  // rows of one tile (block_m <= 256)
+    const float* __restrict__ dl, const int32_t* __restrict__ offsets, int E, int bm,
+    float* __restrict__ partial) {
+  __shared__ int64_t tok[256];  // rows of one piece (block_m <= 256)
   __shared__ float dv[256];
+  __shared__ int piece_row0, piece_rows;
   const int tile = blockIdx.x;
-  if (tile >= *num_tiles) return;
-  const int row0 = tiles[3 * tile + 1], rows = tiles[3 * tile + 2];
+  if (threadIdx.x == 0) {
+    int n = 0, r0 = 0, nr = 0;
+    for (int e = 0; e < E; ++e) {
+      const int cnt = offsets[e + 1] - offsets[e];
+      const int np = (cnt + bm - 1) / bm;
+      if (tile < n + np) {
+        const int r = (tile - n) * bm;
+        r0 = offsets[e] + r;
+        nr = cnt - r < bm ? cnt - r : bm;
+        break;
+      }
+      n += np;
+    }
+    piece_row0 = r0;
+    piece_rows = nr;
+  }
+  __syncthreads();
+  const int row0 = piece_row0, rows = piece_rows;
+  if (rows == 0) return;
   for (int r = threadIdx.x; r < rows; r += kRowThreads) {
     const int32_t s = perm[row0 + r];
     tok[r] = s / topk;
@@ -180,7 +204,13 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
       const int e = topk_idx[t * k + i];
       const float li = dl[t * k + i];
       float v[N], wv[N];
-      V16<T>::load(dxs + slot * d + c, v);
+      if (slot >= 0) {
+        V16<T>::load(dxs + slot * d + c, v);
+      } else {
+        // dropped by capacity routing: only the router term
+#pragma unroll
+        for (int q = 0; q < N; ++q) v[q] = 0.0f;
+      }
 #pragma unroll
       for (int q = 0; q < N; q += 4) {
         const float4 w4 = *reinterpret_cast<const float4*>(wrT + static_cast<int64_t>(e) * d + c + q);
@@ -340,8 +370,8 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
              static_cast<const T*>(y_sorted), r.topk_w, r.inv_perm, dY, dl);
   // a12: router weight gradient (tile partials, then a per-expert ordered sum)
   MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
-             dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl, r.tiles,
-             r.num_tiles, rpart);
+             dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
+             r.expert_offsets, E, p.block_m, rpart);
   MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
              r.expert_offsets, E, p.block_m, d, g.w_router);
   // a13 + a15: dgrad GEMMs
@@ -357,6 +387,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     a.M = h;
     a.N = d;
     a.row_offsets = r.expert_offsets;
+    a.cap = p.capacity;
     a.c = g.w_down;
     a.nsplit = d;
     a.ldc = d;
@@ -372,6 +403,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     b.M = d;
     b.N = 2 * h;
     b.row_offsets = r.expert_offsets;
+    b.cap = p.capacity;
     b.c = g.w_gate;
     b.c2 = g.w_up;
     b.nsplit = h;

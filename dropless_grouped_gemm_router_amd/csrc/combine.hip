@@ -4,7 +4,8 @@
 // rows, accumulates in fp32 in rank order i = 0..k-1 and writes the row
 // once. No atomics, so the result is deterministic. The stage is bound by
 // HBM bandwidth: each lane moves 16-byte pieces of a row. k <= 8 takes a
-// variant with all row loads of a piece in flight at once.
+// variant with all row loads of a piece in flight at once. Slots dropped by
+// capacity routing (inv_perm -1) are left out.
 #include "common.h"
 
 namespace moe {
@@ -67,15 +68,18 @@ __global__ __launch_bounds__(kCombThreads) void combine_k_kernel(
   for (int c = lane * N; c < d; c += 64 * N) {
     float v[K][N], sv[N];
 #pragma unroll
-    for (int i = 0; i < K; ++i) Vec<T>::load(y + row[i] * d + c, v[i]);
+    for (int i = 0; i < K; ++i)
+      if (row[i] >= 0) Vec<T>::load(y + row[i] * d + c, v[i]);
     if (kShared) Vec<T>::load(shared_out + t * d + c, sv);
     float acc[N];
 #pragma unroll
     for (int q = 0; q < N; ++q) acc[q] = 0.0f;
 #pragma unroll
     for (int i = 0; i < K; ++i)
+      if (row[i] >= 0) {
 #pragma unroll
-      for (int q = 0; q < N; ++q) acc[q] = __builtin_fmaf(wi[i], v[i][q], acc[q]);
+        for (int q = 0; q < N; ++q) acc[q] = __builtin_fmaf(wi[i], v[i][q], acc[q]);
+      }
     if (kShared) {
 #pragma unroll
       for (int q = 0; q < N; ++q) acc[q] += sv[q];
@@ -98,6 +102,7 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     for (int q = 0; q < N; ++q) acc[q] = 0.0f;
     for (int i = 0; i < k; ++i) {
       const int64_t row = inv_perm[t * k + i];
+      if (row < 0) continue;
       const float wi = w[t * k + i];
       float v[N];
       Vec<T>::load(y + row * d + c, v);

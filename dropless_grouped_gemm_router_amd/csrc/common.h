@@ -119,7 +119,7 @@ hipError_t launch_route(int dtype, const void* x, const float* w_router, int64_t
                         int k, int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 size_t permute_ws_bytes(int64_t S, int E);
-hipError_t launch_permute(int64_t T, int k, int E, int bm, const int32_t* topk_idx,
+hipError_t launch_permute(int64_t T, int k, int E, int bm, int cap, const int32_t* topk_idx,
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tiles,
                           int32_t* num_tiles, void* ws, hipStream_t s);
 

@@ -263,8 +263,8 @@ hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, con
   hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
                               r.topk_idx, r.topk_w, s);
   if (e != hipSuccess) return e;
-  e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, r.topk_idx, r.expert_offsets, r.perm,
-                     r.inv_perm, r.tiles, r.num_tiles, ws, s);
+  e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, p.capacity, r.topk_idx,
+                     r.expert_offsets, r.perm, r.inv_perm, r.tiles, r.num_tiles, ws, s);
   if (e != hipSuccess) return e;
   void* shared_out = p.d_shared > 0 && !L.fused ? W + L.shared_out : nullptr;
   void* x_sorted = dispatch == MOE_DISPATCH_SORTED ? W + L.x_sorted : nullptr;

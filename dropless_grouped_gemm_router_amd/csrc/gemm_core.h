@@ -70,7 +70,8 @@ __device__ __forceinline__ float round_to(float v, const float*) { return v; }
 // Fused gather-sum for four consecutive columns n.. of token t, in the
 // combine stage's order: fp32 multiply-adds over ranks 0..k-1 from zero,
 // then the (already rounded) dense value v added. idx and wt hold the
-// token's sorted rows and weights.
+// token's sorted rows and weights; a row of -1 (dropped by capacity routing)
+// is left out.
 template <typename T>
 __device__ __forceinline__ void combine4(const GemmArgs& p, int64_t t, int n, const float (&v)[4],
                                          const int (&idx)[kCombineMaxK],
@@ -79,11 +80,11 @@ __device__ __forceinline__ void combine4(const GemmArgs& p, int64_t t, int n, co
   float yv[kCombineMaxK][4];
 #pragma unroll
   for (int i = 0; i < kCombineMaxK; ++i)
-    if (i < p.gk) load4(y + static_cast<int64_t>(idx[i]) * p.ldc + n, yv[i]);
+    if (i < p.gk && idx[i] >= 0) load4(y + static_cast<int64_t>(idx[i]) * p.ldc + n, yv[i]);
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int i = 0; i < kCombineMaxK; ++i)
-    if (i < p.gk) {
+    if (i < p.gk && idx[i] >= 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(wt[i], yv[i][q], acc[q]);
     }
@@ -465,6 +466,8 @@ struct WgradArgs {
   int64_t ldb;
   int M, N;
   const int32_t* row_offsets;  // grouped mode: [groups + 1]
+  int cap;                     // grouped mode: rows per group past which rows are
+                               // dropped (capacity routing); 0 = none
   int64_t rows_total;          // dense mode
   int splits;                  // dense mode
   float* c;
@@ -577,6 +580,7 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const WgradArgs p) {
   } else {
     r0 = p.row_offsets[grp];
     r1 = p.row_offsets[grp + 1];
+    if (p.cap > 0 && r1 - r0 > p.cap) r1 = r0 + p.cap;
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;

@@ -174,7 +174,8 @@ __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int6
 // wave's comb area holds each row's sorted rows ([64][k] int32) and weights
 // ([64][k] fp32 at byte 2048). Each 16-byte output piece is the combine
 // stage's sum, in its order: fp32 multiply-adds over ranks 0..k-1 from zero,
-// then the dense value. All k row loads of a piece are issued before use.
+// then the dense value; rows of -1 (dropped by capacity routing) are left
+// out. All k row loads of a piece are issued before use.
 __device__ __forceinline__ void wide_drain_combine(const GemmArgs& p, const char* region,
                                                    const char* comb, int64_t orow, int col,
                                                    int rows, int lane) {
@@ -198,11 +199,12 @@ __device__ __forceinline__ void wide_drain_combine(const GemmArgs& p, const char
     u32x4 yv[kCombineMaxK];
 #pragma unroll
     for (int i = 0; i < kCombineMaxK; ++i)
-      if (i < K) yv[i] = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(idx[i]) * p.ldc + col + c * 8);
+      if (i < K && idx[i] >= 0)
+        yv[i] = *reinterpret_cast<const u32x4*>(y + static_cast<int64_t>(idx[i]) * p.ldc + col + c * 8);
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int i = 0; i < kCombineMaxK; ++i)
-      if (i < K) {
+      if (i < K && idx[i] >= 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           acc[2 * q] = __builtin_fmaf(wt[i], bf16lo(yv[i][q]), acc[2 * q]);

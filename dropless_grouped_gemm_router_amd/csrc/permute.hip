@@ -47,10 +47,17 @@ __global__ __launch_bounds__(kPermThreads) void count_kernel(const int32_t* __re
 
 constexpr int kScanThreads = 1024;
 
+// Rows of an expert with `count` slots that capacity routing keeps (cap 0:
+// all of them).
+__device__ __forceinline__ int32_t kept_rows(int32_t count, int cap) {
+  return (cap > 0 && count > cap) ? cap : count;
+}
+
 // One workgroup: in-place exclusive scan of blk_counts[E * nblk], then the
 // expert offsets and the tile list.
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ blk_counts,
-                                                            int nblk, int E, int bm, int64_t S,
+                                                            int nblk, int E, int bm, int cap,
+                                                            int64_t S,
                                                             int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ tiles,
                                                             int32_t* __restrict__ num_tiles) {
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
     int32_t nt = 0;
     for (int e = 0; e < E; ++e) {
       tile_off[e] = nt;
-      nt += (off[e + 1] - off[e] + bm - 1) / bm;
+      nt += (kept_rows(off[e + 1] - off[e], cap) + bm - 1) / bm;
     }
     tile_off[E] = nt;
     *num_tiles = nt;
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += kScanThreads) offsets[e] = off[e];
   // Tile n of expert e covers rows [off[e] + (n - tile_off[e]) * bm, ...),
-  // at most bm of them.
+  // at most bm of them, within the expert's kept rows.
   const int32_t nt = tile_off[E];
   for (int32_t n = threadIdx.x; n < nt; n += kScanThreads) {
     int lo = 0, hi = E - 1;  // last e with tile_off[e] <= n
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
     const int32_t r = (n - tile_off[e]) * bm;
     tiles[3 * n + 0] = e;
     tiles[3 * n + 1] = off[e] + r;
-    tiles[3 * n + 2] = min(bm, off[e + 1] - off[e] - r);
+    tiles[3 * n + 2] = min(bm, kept_rows(off[e + 1] - off[e], cap) - r);
   }
 }
 
@@ -160,7 +167,8 @@ __device__ __forceinline__ uint64_t same_expert_mask(int e) {
 __global__ __launch_bounds__(kPermThreads) void scatter_kernel(const int32_t* __restrict__ idx,
                                                                int64_t S, int E, int nblk,
                                                                const int32_t* __restrict__ blk_base,
-                                                               int32_t* __restrict__ perm,
+                                                               const int32_t* __restrict__ offsets,
+                                                               int cap, int32_t* __restrict__ perm,
                                                                int32_t* __restrict__ inv_perm) {
   __shared__ int32_t wave_cnt[kPermThreads / 64][kMaxE];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -200,7 +208,8 @@ __global__ __launch_bounds__(kPermThreads) void scatter_kernel(const int32_t* __
       const int32_t base = wave_cnt[wave][e];
       const int32_t pos = base + rank;
       perm[pos] = static_cast<int32_t>(s);
-      inv_perm[s] = pos;
+      // Capacity routing drops every slot past the expert's first cap.
+      inv_perm[s] = (cap > 0 && pos - offsets[e] >= cap) ? -1 : pos;
     }
     // All lanes have read their base (the read above precedes this point
     // in the wave's in-order LDS queue); the last lane of each expert group
@@ -218,7 +227,7 @@ size_t permute_ws_bytes(int64_t S, int E) {
   return align_up(sizeof(int32_t) * static_cast<size_t>(nblk) * E, 256);
 }
 
-hipError_t launch_permute(int64_t T, int k, int E, int bm, const int32_t* topk_idx,
+hipError_t launch_permute(int64_t T, int k, int E, int bm, int cap, const int32_t* topk_idx,
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tiles,
                           int32_t* num_tiles, void* ws, hipStream_t s) {
   const int64_t S = T * k;
@@ -226,10 +235,10 @@ hipError_t launch_permute(int64_t T, int k, int E, int bm, const int32_t* topk_i
   int32_t* blk = static_cast<int32_t*>(ws);
   MOE_LAUNCH("permute_count", count_kernel, dim3(nblk), dim3(kPermThreads), 0, s, topk_idx, S, E, nblk,
                      blk);
-  MOE_LAUNCH("permute_scan", scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, nblk, E, bm, S, offsets,
-                     tiles, num_tiles);
+  MOE_LAUNCH("permute_scan", scan_kernel, dim3(1), dim3(kScanThreads), 0, s, blk, nblk, E, bm, cap, S,
+             offsets, tiles, num_tiles);
   MOE_LAUNCH("permute_scatter", scatter_kernel, dim3(nblk), dim3(kPermThreads), 0, s, topk_idx, S, E, nblk,
-                     blk, perm, inv_perm);
+             blk, offsets, cap, perm, inv_perm);
   return hipGetLastError();
 }
 

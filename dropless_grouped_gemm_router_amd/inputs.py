@@ -127,10 +127,20 @@ class Problem:
     # Routing skew of the generated router (0 = uniform routing). Not a layer
     # argument: it only shapes the synthetic router, see make_inputs.
     skew: float = 0.0
+    # Capacity routing (kernel_gmm_gpu.json "routing": "capacity"): at most
+    # this many token-slots per expert, the first in flat slot order; 0 =
+    # dropless. A layer argument (moe_problem.capacity).
+    capacity: int = 0
 
     @property
     def slots(self) -> int:
         return self.tokens * self.top_k
+
+
+def capacity_for(p: Problem, factor: float) -> int:
+    """Per-expert capacity of a capacity factor: ceil(factor * tokens *
+    top_k / experts), the mean load scaled (at least 1)."""
+    return max(1, math.ceil(factor * p.tokens * p.top_k / p.experts))
 
 
 @dataclasses.dataclass

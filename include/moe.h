@@ -76,6 +76,14 @@ typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
  * route piece takes bf16 tokens with an fp32 router and the combine piece
  * bf16 expert outputs with fp32 weights).
  *
+ * capacity (kernel_gmm_gpu.json records, field "routing": "capacity"
+ * against "dropless"): 0 routes every token-slot (dropless). capacity > 0
+ * caps each expert at that many token-slots, the first ones in flat slot
+ * order t*top_k + i (ascending token): the rest are dropped, contribute
+ * nothing to out and no gradient to their expert's weights, and the kept
+ * combine weights are not renormalised. The pages name the variant but give
+ * neither the capacity nor the drop rule; this is the rule implemented.
+ *
  * Supported (else MOE_ERR_UNSUPPORTED): 1 <= experts <= 64,
  * 1 <= top_k <= experts, d_model a multiple of 128 (at most 8192),
  * d_hidden and d_shared multiples of 64 (d_shared may be 0), block_m in
@@ -90,6 +98,7 @@ typedef struct {
   int32_t d_shared; /* 0 = no shared expert */
   int32_t dtype;    /* moe_dtype */
   int32_t block_m;
+  int32_t capacity; /* max token-slots per expert; 0 = dropless; < 0 is MOE_ERR_INVALID */
 } moe_problem;
 
 /* Layer weights (device, caller-owned, read only). */
@@ -112,8 +121,9 @@ typedef struct {
   float* topk_w;           /* [tokens, top_k]: renormalised combine weights */
   int32_t* expert_offsets; /* [experts + 1]: first sorted row of each expert; [experts] = S */
   int32_t* perm;           /* [S]: sorted row -> flat slot; rows of one expert in ascending slot order */
-  int32_t* inv_perm;       /* [S]: flat slot -> sorted row */
-  int32_t* tiles;          /* [moe_max_tiles(), 3]: (expert, first sorted row, rows <= block_m) */
+  int32_t* inv_perm;       /* [S]: flat slot -> sorted row; -1 if capacity dropped the slot */
+  int32_t* tiles;          /* [moe_max_tiles(), 3]: (expert, first sorted row, rows <= block_m),
+                              covering each expert's kept rows */
   int32_t* num_tiles;      /* [1]: number of valid entries of tiles */
 } moe_routing;
 
@@ -188,7 +198,10 @@ int moe_route(const moe_problem* p, const void* x, const float* w_router, moe_ro
  * expert (within an expert, slots keep ascending flat order, hence
  * ascending token order) and the tile list: for each expert in ascending
  * order, its rows cut into pieces of block_m rows, the last one partial.
- * Empty experts have no tile. workspace: >= moe_workspace_bytes(p, 0).
+ * Empty experts have no tile. With capacity > 0 an expert's sorted rows
+ * past its first `capacity` are dropped: no tile covers them, and their
+ * slots get inv_perm -1 (perm and expert_offsets still list every slot).
+ * workspace: >= moe_workspace_bytes(p, 0).
  */
 int moe_permute(const moe_problem* p, moe_routing* r, void* workspace, size_t workspace_bytes,
                 void* stream);
@@ -214,7 +227,8 @@ int moe_ffn_fwd(const moe_problem* p, const void* x, const moe_weights* w, const
  * Stage "unpermute_combine" (kernel_gmm_gpu.json "pieces" suite):
  *   out[t] = sum_i topk_w[t,i] * y_sorted[inv_perm[t*top_k + i]] + shared_out[t]
  * a gather-sum in fp32 (one writer per output row, no atomics), stored in
- * dtype. shared_out may be NULL (no shared term).
+ * dtype. shared_out may be NULL (no shared term). Slots with inv_perm -1
+ * (dropped by capacity) are left out of the sum.
  */
 int moe_combine(const moe_problem* p, const void* y_sorted, const moe_routing* r,
                 const void* shared_out, void* out, void* stream);

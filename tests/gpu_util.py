@@ -13,6 +13,22 @@ from oracle import oracle
 TOL = {"fp32": 1e-4, "bf16": 2e-2}
 
 
+def pid(p: Problem) -> str:
+    """Test id of a problem."""
+    return (f"T{p.tokens}E{p.experts}k{p.top_k}d{p.d_model}h{p.d_hidden}s{p.d_shared}{p.dtype}"
+            f"bm{p.block_m}" + (f"skew{p.skew}" if p.skew else "")
+            + (f"cap{p.capacity}" if p.capacity else ""))
+
+
+def keep_of(p: Problem, idx):
+    """[T, k] flags of the slots capacity routing keeps (None: dropless),
+    from the oracle's permutation."""
+    if not p.capacity:
+        return None
+    r = oracle.permute(idx, p.experts, p.block_m, capacity=p.capacity)
+    return oracle.keep_mask(r, p.tokens, p.top_k)
+
+
 def note(msg):
     print(msg, flush=True)
     sys.stdout.flush()

@@ -48,6 +48,8 @@ def test_param_count_and_tiles():
     (dict(tokens=-1), B.MOE_ERR_INVALID),
     (dict(dtype=7), B.MOE_ERR_INVALID),
     (dict(d_shared=-64), B.MOE_ERR_INVALID),
+    (dict(capacity=-1), B.MOE_ERR_INVALID),
+    (dict(capacity=1), B.MOE_OK),
     (dict(experts=65, top_k=2), B.MOE_ERR_UNSUPPORTED),
     (dict(block_m=48), B.MOE_ERR_UNSUPPORTED),
     (dict(block_m=512), B.MOE_ERR_UNSUPPORTED),

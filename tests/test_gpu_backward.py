@@ -7,7 +7,7 @@ from dropless_grouped_gemm_router_amd import binding as B
 from dropless_grouped_gemm_router_amd.inputs import Problem, WORKLOADS
 from oracle import oracle
 
-from gpu_util import TOL, Case, note, to_np
+from gpu_util import TOL, Case, keep_of, note, pid, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -28,7 +28,8 @@ def check_grads(c: Case, gx, g, nthreads=0):
     _, idx_ref, w = oracle.route(v["x"], v["w_router"], p.top_k, nthreads)
     assert np.array_equal(idx, idx_ref)
     ref = oracle.backward(v["x"], v["w_router"], v["w_gate"], v["w_up"], v["w_down"],
-                          v["grad_out"], idx_ref, w, *c.shared(), nthreads=nthreads)
+                          v["grad_out"], idx_ref, w, *c.shared(), nthreads=nthreads,
+                          keep=keep_of(p, idx_ref))
     errs = {"x": oracle.rel_err(to_np(gx), ref["x"])}
     for n in GRAD_NAMES:
         if n in g:
@@ -50,10 +51,16 @@ SMALL = [
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256),
     Problem(700, 4, 2, 256, 256, 128, "fp32", 256),
     Problem(2000, 64, 8, 256, 128, 128, "bf16", 128, skew=0.9),
+    # capacity routing: dropped slots give no expert gradient but still a
+    # router gradient
+    Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),
+    Problem(517, 16, 4, 256, 128, 128, "fp32", 32, capacity=100),
+    Problem(2000, 64, 8, 256, 128, 128, "bf16", 128, skew=0.9, capacity=200),
+    Problem(300, 8, 2, 256, 128, 0, "bf16", 64, capacity=1),
 ]
 
 
-@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}" + (f"skew{p.skew}" if p.skew else ""))
+@pytest.mark.parametrize("p", SMALL, ids=pid)
 def test_backward_small_elementwise(p):
     note(f"backward small {p}")
     c = Case(p, seed=11, training=True)

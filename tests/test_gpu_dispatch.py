@@ -13,7 +13,7 @@ from dropless_grouped_gemm_router_amd import binding as B
 from dropless_grouped_gemm_router_amd.inputs import Problem, WORKLOADS
 from oracle import oracle
 
-from gpu_util import TOL, Case, note, to_np
+from gpu_util import TOL, Case, keep_of, note, pid, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -35,12 +35,10 @@ CASES = [
     Problem(300, 8, 2, 256, 128, 0, "bf16", 64),
     Problem(1, 4, 2, 128, 64, 64, "bf16", 32),
     Problem(3000, 64, 8, 256, 128, 128, "bf16", 256, skew=0.9),
+    # capacity routing: dropped slots are left out of every variant's combine
+    Problem(3000, 64, 8, 256, 128, 128, "bf16", 256, skew=0.9, capacity=300),
+    Problem(517, 16, 4, 384, 192, 128, "bf16", 128, capacity=100),
 ]
-
-
-def pid(p):
-    return (f"T{p.tokens}E{p.experts}k{p.top_k}d{p.d_model}h{p.d_hidden}s{p.d_shared}"
-            f"{p.dtype}bm{p.block_m}" + (f"skew{p.skew}" if p.skew else ""))
 
 
 def bits_equal(a, b) -> bool:
@@ -61,7 +59,11 @@ def assert_same_forward(ref: B.Buffers, got: B.Buffers, n_tiles: int, training=F
     for k in ("topk_idx", "topk_w", "expert_offsets", "perm", "inv_perm", "num_tiles"):
         assert bits_equal(ref.routing[k], got.routing[k]), k
     assert bits_equal(ref.routing["tiles"][:n_tiles], got.routing["tiles"][:n_tiles])
-    assert bits_equal(ref.y_sorted, got.y_sorted)
+    # every row of a kept slot (rows of slots dropped by capacity routing are
+    # never written)
+    rows = ref.routing["inv_perm"]
+    rows = rows[rows >= 0].long()
+    assert bits_equal(ref.y_sorted[rows], got.y_sorted[rows])
     assert bits_equal(ref.out, got.out)
     if training:
         assert bits_equal(ref.saved, got.saved)
@@ -79,7 +81,7 @@ def test_dispatch_matches_staged_and_oracle(p, dispatch):
     idx = got.routing["topk_idx"].cpu().numpy()
     w = got.routing["topk_w"].cpu().numpy().astype(np.float64)
     ref = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx, w,
-                              *c.shared())
+                              *c.shared(), keep=keep_of(p, idx))
     assert oracle.rel_err(to_np(got.out), ref) < TOL[p.dtype]
 
 

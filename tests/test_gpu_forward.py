@@ -6,7 +6,7 @@ import pytest
 from dropless_grouped_gemm_router_amd.inputs import Problem, WORKLOADS
 from oracle import oracle
 
-from gpu_util import TOL, Case, note, to_np
+from gpu_util import TOL, Case, keep_of, note, pid, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -18,7 +18,7 @@ def check_routing(c: Case, nthreads=0):
     g = c.routing_np()
     assert np.array_equal(g["topk_idx"], idx)
     assert np.max(np.abs(g["topk_w"] - w)) < 2e-6
-    r = oracle.permute(idx, p.experts, p.block_m)
+    r = oracle.permute(idx, p.experts, p.block_m, capacity=p.capacity)
     assert np.array_equal(g["offsets"], r["offsets"])
     assert np.array_equal(g["perm"], r["perm"])
     assert np.array_equal(g["inv_perm"], r["inv_perm"])
@@ -44,20 +44,32 @@ SMALL = [
     # skewed routing (uneven expert loads, nearly empty experts)
     Problem(3000, 64, 8, 256, 128, 128, "bf16", 256, skew=0.9),
     Problem(3000, 64, 8, 256, 128, 0, "bf16", 64, skew=0.9),
+    # capacity routing: the busier experts drop their last slots
+    Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),
+    Problem(517, 16, 4, 256, 192, 128, "fp32", 32, capacity=100),
+    Problem(3000, 64, 8, 256, 128, 0, "bf16", 64, skew=0.9, capacity=375),
+    Problem(3000, 64, 8, 256, 128, 128, "bf16", 256, skew=0.9, capacity=300),
+    Problem(300, 8, 2, 256, 128, 0, "bf16", 128, capacity=1),
 ]
 
 
-@pytest.mark.parametrize("p", SMALL, ids=lambda p: f"T{p.tokens}E{p.experts}k{p.top_k}h{p.d_hidden}s{p.d_shared}{p.dtype}bm{p.block_m}" + (f"skew{p.skew}" if p.skew else ""))
+@pytest.mark.parametrize("p", SMALL, ids=pid)
 def test_forward_small_elementwise(p):
     note(f"forward small {p}")
     c = Case(p, seed=7)
     out = c.forward()
     idx, w, r = check_routing(c)
+    keep = keep_of(p, idx)
     ref, y = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx, w,
-                                 *c.shared(), want_y=True)
-    ys = to_np(c.buf.y_sorted)
-    # sorted expert outputs: row inv_perm[s] holds the unweighted output of flat slot s
-    assert oracle.rel_err(ys[r["inv_perm"]], y) < TOL[p.dtype]
+                                 *c.shared(), want_y=True, keep=keep)
+    # sorted expert outputs: row inv_perm[s] holds the unweighted output of
+    # flat slot s (kept slots only; rows of dropped ones are never written)
+    kept = r["inv_perm"] >= 0
+    if p.capacity:
+        assert not kept.all()
+    import torch
+    ys = to_np(c.buf.y_sorted[torch.from_numpy(r["inv_perm"][kept].astype(np.int64)).cuda()])
+    assert oracle.rel_err(ys, y[kept]) < TOL[p.dtype]
     if p.d_shared:
         sref = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx,
                                    np.zeros_like(w), *c.shared())
