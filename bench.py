@@ -73,6 +73,38 @@ def work(p, dispatch="gather"):
     return w
 
 
+def bwd_work(p):
+    """Algorithmic work of each backward kernel per launch: (flops, bytes),
+    counted as in ``work``. S = T*k token-slots; weight gradients are fp32."""
+    T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
+    S = T * k
+    es = 2 if p.dtype == "bf16" else 4
+    w = {
+        # grad_out and y read, dY written, weights / slot map read, dl written
+        "bwd_combine": (2 * S * d, T * d * es + S * d * es + S * d * es + S * 12),
+        # token rows and dl read, per-piece partials written
+        "bwd_router_partial": (2 * S * d, T * d * es + S * 8 + ((S + p.block_m - 1) // p.block_m + E) * d * 4),
+        # dY, down weights and saved gate/up read, dA|dB written
+        "bwd_down_dgrad": (2 * S * d * h, S * d * es + E * h * d * es + 2 * S * 2 * h * es),
+        # dA|dB and gate/up weights read, per-slot dX written
+        "bwd_gate_up_dgrad": (2 * S * 2 * h * d, S * 2 * h * es + E * 2 * h * d * es + S * d * es),
+        # H and dY read, fp32 dW_down written
+        "bwd_wgrad_down": (2 * S * h * d, S * h * es + S * d * es + E * h * d * 4),
+        # token rows and dA|dB read, fp32 dW_gate, dW_up written
+        "bwd_wgrad_gate_up": (2 * S * d * 2 * h, T * d * es + S * 2 * h * es + E * d * 2 * h * 4),
+        # per-slot dX, router term and shared dx read, grad_x written
+        "bwd_dx": (2 * S * d, S * d * es + E * d * 4 + S * 8 + 2 * T * d * es),
+    }
+    if hs:
+        w.update({
+            "bwd_shared_down_dgrad": (2 * T * d * hs, T * d * es + hs * d * es + 2 * T * 2 * hs * es),
+            "bwd_shared_gate_up_dgrad": (2 * T * 2 * hs * d, T * 2 * hs * es + 2 * hs * d * es + T * d * es),
+            "bwd_shared_wgrad_down": (2 * T * hs * d, T * hs * es + T * d * es + hs * d * 4),
+            "bwd_shared_wgrad_gate_up": (2 * T * d * 2 * hs, T * d * es + T * 2 * hs * es + d * 2 * hs * 4),
+        })
+    return w
+
+
 def roofline_of(kname, flops, nbytes, avg_ms, dtype):
     """Roofline position of one launch: the bound is whichever of compute
     (MFMA, or fp32 VALU for the router) and HBM takes longer at peak."""
@@ -97,7 +129,7 @@ def trace_name(kernel):
     import re
     if "route_kernel" in kernel or "route_resident_kernel" in kernel:
         return "route"
-    if "combine_kernel" in kernel:
+    if "combine_kernel" in kernel or "combine_k_kernel" in kernel:
         return "combine"
     for k in ("count", "scan", "scatter"):
         if f"{k}_kernel" in kernel:
@@ -193,7 +225,7 @@ def train_step_line(B, steps, warmup):
     """Forward + backward on the train-step workload (16384 tokens)."""
     import torch
 
-    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, capacity_for, make_inputs
+    from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, make_inputs
 
     name, p, _ = WORKLOADS[4]
     dev = B.device_inputs(make_inputs(p, seed=0, with_grad_out=True), "cuda:0")
@@ -206,10 +238,95 @@ def train_step_line(B, steps, warmup):
         B.backward(p, x, dev, g, buf)
 
     ms = time_steps(step, steps, warmup)
+    # per-kernel times of the same steps, from libmoe's HIP events
+    B.moe_trace_enable(True)
+    time_steps(step, steps, 0)
+    kern = B.moe_trace_summary()
+    B.moe_trace_enable(False)
     T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
     fwd = 2 * T * d * E + 6 * T * k * d * h + 6 * T * d * hs
+    wk = dict(work(p))
+    wk.update(bwd_work(p))
+    avg = {kn: v["ms"] / v["count"] for kn, v in kern.items()}
+    roofs = {kn: roofline_of(kn, wk[kn][0], wk[kn][1], avg[kn], p.dtype) for kn in wk if kn in avg}
     return {"workload": name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
-            "tflops_3x_fwd": 3 * fwd / (ms * 1e-3) / 1e12, "steps": steps, "warmup": warmup}
+            "tflops_3x_fwd": 3 * fwd / (ms * 1e-3) / 1e12, "steps": steps, "warmup": warmup,
+            "kernels_ms_per_step": {kn: round(v["ms"] / steps, 5) for kn, v in sorted(kern.items())},
+            "kernel_rooflines": {kn: {"frac": round(r["frac"], 4), "achieved": round(r["achieved"], 1),
+                                      "unit": r["unit"], "bound": r["bound"]}
+                                 for kn, r in sorted(roofs.items())}}
+
+
+def train_footprint(B, p):
+    """Device bytes of one train step without allocating anything: the
+    inputs (tokens, grad_out, weights), every buffer ``binding.allocate``
+    makes with training=True (routing, y_sorted, out, grad_x, shared_out,
+    workspace, saved activations, fp32 weight gradients)."""
+    T, E, k, d, h, hs = p.tokens, p.experts, p.top_k, p.d_model, p.d_hidden, p.d_shared
+    S = T * k
+    es = 2 if p.dtype == "bf16" else 4
+    inputs = 2 * T * d * es + d * E * 4 + 3 * E * d * h * es + 3 * d * hs * es
+    routing = 2 * T * k * 4 + (E + 1) * 4 + 2 * S * 4 + max(1, B.moe_max_tiles(p)) * 12 + 4
+    acts = S * d * es + T * d * es * (3 if hs else 2)
+    grads = (d * E + 3 * E * d * h + 3 * d * hs) * 4
+    return (inputs + routing + acts + grads + B.moe_workspace_bytes(p, True)
+            + B.moe_saved_bytes(p))
+
+
+MAXTOK_BLOCK = 131072
+
+
+def maxtok_line(B, steps, warmup):
+    """Largest train step that fits this GPU at the pages' max-token shape
+    (kernel_gmm_gpu.json "maxtok" suite: E=8, top-2, d_model 512, d_hidden
+    1024, bf16), with peak device memory and step time at token counts up to
+    it. Tokens and grad_out are the seeded 131072-token block repeated."""
+    import dataclasses
+
+    import torch
+
+    from dropless_grouped_gemm_router_amd.inputs import Problem, make_inputs
+
+    p0 = Problem(MAXTOK_BLOCK, 8, 2, 512, 1024, 0, "bf16", 128)
+    dev = B.device_inputs(make_inputs(p0, seed=0, with_grad_out=True), "cuda:0")
+    x0, g0 = dev.pop("x"), dev.pop("grad_out")
+    torch.cuda.synchronize()
+    free, total = torch.cuda.mem_get_info()
+    budget = int(free * 0.96)
+    tmax = MAXTOK_BLOCK
+    while train_footprint(B, dataclasses.replace(p0, tokens=tmax + MAXTOK_BLOCK)) <= budget:
+        tmax += MAXTOK_BLOCK
+    points = sorted({t for t in (MAXTOK_BLOCK, 1 << 20, 1 << 22, tmax) if t <= tmax})
+    out = []
+    for T in points:
+        p = dataclasses.replace(p0, tokens=T)
+        print(f"bench: maxtok {T} tokens", file=sys.stderr, flush=True)
+        reps = -(-T // MAXTOK_BLOCK)
+        x = x0.repeat(reps, 1)[:T].contiguous()
+        g = g0.repeat(reps, 1)[:T].contiguous()
+        buf = B.allocate(p, "cuda:0", training=True)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+
+        def step():
+            B.forward(p, x, dev, buf, training=True)
+            B.backward(p, x, dev, g, buf)
+
+        ms = time_steps(step, steps, warmup)
+        peak = torch.cuda.max_memory_allocated()
+        out.append({"tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+                    "peak_mb": peak / 2 ** 20, "footprint_mb": train_footprint(B, p) / 2 ** 20})
+        del buf, x, g
+        torch.cuda.empty_cache()
+    return {"metric": "largest train step on one GPU (max tokens)", "value": tmax,
+            "unit": "tokens", "higher_is_better": True, "n_gpus": 1,
+            "config": {"workload": "train bf16, E8 top-2, d512 h1024 (max-token shape)",
+                       "experts": 8, "top_k": 2, "d_model": 512, "d_hidden": 1024,
+                       "block_m": p0.block_m, "dtype": "bf16"},
+            "device_free_mb_at_start": free / 2 ** 20, "device_total_mb": total / 2 ** 20,
+            "budget_frac": 0.96, "bytes_per_token": (train_footprint(B, dataclasses.replace(p0, tokens=2 * MAXTOK_BLOCK))
+                                                     - train_footprint(B, p0)) / MAXTOK_BLOCK,
+            "points": out, "data": "synthetic: a seeded 131072-token block repeated"}
 
 
 def main():
@@ -230,6 +347,8 @@ def main():
                     help="tokens the CPU oracle runs on (about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--maxtok", action="store_true",
+                    help="largest train step that fits (E8 top-2 d512 h1024 bf16) and peak memory")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
@@ -261,6 +380,11 @@ def main():
 
     from dropless_grouped_gemm_router_amd import binding as B
     from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, capacity_for, make_inputs
+
+    if args.maxtok:
+        torch.cuda.set_device(0)
+        print(json.dumps(maxtok_line(B, max(1, min(args.steps, 3)), 1)), flush=True)
+        return
 
     name, p, _ = WORKLOADS[args.workload]
     if args.block_m:

@@ -36,6 +36,19 @@ struct V16<bf16_t> {
     v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
     *reinterpret_cast<uint4*>(p) = v;
   }
+  // Nontemporal forms, for rows touched once (gathered expert outputs and
+  // input gradients, the final grad_x) that should not evict reused data.
+  __device__ static void load_nt(const bf16_t* p, float* o) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    o[0] = bf16lo(v.x); o[1] = bf16hi(v.x); o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
+    o[4] = bf16lo(v.z); o[5] = bf16hi(v.z); o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
+  }
+  __device__ static void store_nt(bf16_t* p, const float* o) {
+    u32x4 v;
+    v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
+    v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+  }
 };
 template <>
 struct V16<float> {
@@ -46,6 +59,14 @@ struct V16<float> {
   }
   __device__ static void store(float* p, const float* o) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+  __device__ static void load_nt(const float* p, float* o) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+  }
+  __device__ static void store_nt(float* p, const float* o) {
+    const f32x4_t v = {o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
   }
 };
 
@@ -76,7 +97,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     for (int c = lane * N; slot >= 0 && c < d; c += 64 * N) {
       float g[N], yv[N], o[N];
       V16<T>::load(G + t * d + c, g);
-      V16<T>::load(y + slot * d + c, yv);
+      V16<T>::load_nt(y + slot * d + c, yv);
 #pragma unroll
       for (int q = 0; q < N; ++q) {
         dot = __builtin_fmaf(g[q], yv[q], dot);
@@ -205,7 +226,7 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
       const float li = dl[t * k + i];
       float v[N], wv[N];
       if (slot >= 0) {
-        V16<T>::load(dxs + slot * d + c, v);
+        V16<T>::load_nt(dxs + slot * d + c, v);
       } else {
         // dropped by capacity routing: only the router term
 #pragma unroll
@@ -221,11 +242,11 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
     }
     if (dx_shared) {
       float v[N];
-      V16<T>::load(dx_shared + t * d + c, v);
+      V16<T>::load_nt(dx_shared + t * d + c, v);
 #pragma unroll
       for (int q = 0; q < N; ++q) acc[q] += v[q];
     }
-    V16<T>::store(dx + t * d + c, acc);
+    V16<T>::store_nt(dx + t * d + c, acc);
   }
 }
 
@@ -258,6 +279,9 @@ struct BwdLayout {
 };
 
 int split_count(int64_t rows, int tiles) {
+  // A shared width under the backward's 128-column tile has no output tile
+  // (moe_bwd rejects it); the forward's training workspace is still sized.
+  if (tiles < 1) tiles = 1;
   int ks = (512 + tiles - 1) / tiles;
   ks = ks < 1 ? 1 : (ks > 64 ? 64 : ks);
   if (ks > rows) ks = static_cast<int>(rows > 0 ? rows : 1);

@@ -14,32 +14,38 @@ namespace {
 
 constexpr int kCombThreads = 256;
 
+// One 16-byte piece. Every byte the combine reads or writes is touched
+// once, so its accesses are nontemporal: the sorted expert outputs
+// (S * d_model elements, far beyond the caches) then stream past L2 and
+// the Infinity Cache instead of evicting what the other stages reuse
+// (measured 0.274 -> 0.242 ms at 131072 tokens, E=64, top-8, bf16).
 template <typename T>
-struct Vec;  // one 16-byte piece
+struct Vec;
 template <>
 struct Vec<bf16_t> {
   static constexpr int N = 8;
   __device__ static void load(const bf16_t* p, float* o) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     o[0] = bf16lo(v.x); o[1] = bf16hi(v.x); o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
     o[4] = bf16lo(v.z); o[5] = bf16hi(v.z); o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
   }
   __device__ static void store(bf16_t* p, const float* o) {
-    uint4 v;
+    u32x4 v;
     v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
     v.z = pack_bf16x2(o[4], o[5]); v.w = pack_bf16x2(o[6], o[7]);
-    *reinterpret_cast<uint4*>(p) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
   }
 };
 template <>
 struct Vec<float> {
   static constexpr int N = 4;
   __device__ static void load(const float* p, float* o) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
-    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
   }
   __device__ static void store(float* p, const float* o) {
-    *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
+    const f32x4_t v = {o[0], o[1], o[2], o[3]};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
   }
 };
 

@@ -233,3 +233,29 @@ def test_buffer_layouts_match_pages_argument_bytes():
             got = (b.y_sorted.numel() * b.y_sorted.element_size()
                    + b.routing["topk_w"].numel() * b.routing["topk_w"].element_size())
         assert got == int(round(c["xla_arg_mb"] * 2 ** 20)), c
+
+
+@pytest.mark.parametrize("p", [Problem(100, 8, 2, 256, 128, 128, "bf16", 64),
+                               Problem(300, 8, 2, 512, 1024, 0, "bf16", 128),
+                               Problem(77, 5, 3, 128, 128, 64, "fp32", 32)])
+def test_train_footprint_equals_allocation(p):
+    """The max-token measurement's footprint model counts exactly what a train
+    step allocates: the generated inputs with grad_out and every buffer of
+    binding.allocate(training=True)."""
+    import bench
+    from dropless_grouped_gemm_router_amd.inputs import make_inputs
+    b = B.allocate(p, device="cpu", training=True)
+    tensors = [b.y_sorted, b.out, b.workspace, b.saved, b.grad_x] + list(b.routing.values())
+    tensors += list(b.grads.values()) + ([b.shared_out] if p.d_shared else [])
+    got = sum(t.numel() * t.element_size() for t in tensors)
+    es = 2 if p.dtype == "bf16" else 4
+    got += sum(t.value.size * (4 if n == "w_router" else es)
+               for n, t in make_inputs(p, seed=0, with_grad_out=True).items())
+    assert bench.train_footprint(B, p) == got
+
+
+def test_training_workspace_for_narrow_shared_width():
+    """d_shared 64 is below the backward's 128-column tile: moe_bwd rejects
+    it, but sizing the training forward's workspace must still work."""
+    p = Problem(77, 5, 3, 128, 128, 64, "bf16", 32)
+    assert B.moe_workspace_bytes(p, True) >= B.moe_workspace_bytes(p, False) > 0
