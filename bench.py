@@ -29,7 +29,7 @@ PEAK_VALU_TFLOPS = 78.6
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = ["gemm_core.h", "gemm_wide.h", "gemm_launch.h", "ffn.hip", "route.hip",
-                  "permute.hip", "combine.hip", "common.h"]
+                  "permute.hip", "combine.hip", "common.h", "sort_rows.h"]
 
 
 def kernel_source_hash():

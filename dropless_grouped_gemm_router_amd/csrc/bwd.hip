@@ -11,8 +11,13 @@
 //   dx[t] = sum_i dX_sorted[slot(t,i)] + router term + shared term
 //
 // Every reduction runs in a fixed order with one writer per output (no
-// floating-point atomics), so the gradients are deterministic.
+// floating-point atomics), so the gradients are deterministic. In bf16 the
+// weight gradients take the transposing-LDS-read kernel (gemm_wgrad.h),
+// which reads row ranges: the token rows of dW_gate, dW_up are first copied
+// into expert order, into dY's buffer once dW_down has consumed dY.
 #include "gemm_launch.h"
+#include "gemm_wgrad.h"
+#include "sort_rows.h"
 
 namespace moe {
 
@@ -274,7 +279,7 @@ __global__ __launch_bounds__(kRowThreads) void fill_zero_kernel(float* __restric
 }
 
 struct BwdLayout {
-  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, total;
+  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, total;
   int ks_sd, ks_sgu;
 };
 
@@ -307,6 +312,7 @@ BwdLayout bwd_layout(const moe_problem& p) {
   L.part_sd = o;  o = align_up(o + static_cast<size_t>(L.ks_sd) * hs * d * 4, 256);
   L.part_sgu = o; o = align_up(o + static_cast<size_t>(L.ks_sgu) * d * 2 * hs * 4, 256);
   L.wrT = o;      o = align_up(o + static_cast<size_t>(p.experts) * d * 4, 256);
+  L.zero = o;     o = align_up(o + kTrZeroBytes, 256);
   L.total = o;
   return L;
 }
@@ -321,8 +327,14 @@ void zero(float* p, int64_t n, hipStream_t s) {
 
 
 
+// Weight gradient: bf16 operands without a row gather take the
+// transposing-LDS-read kernel, the rest the register-transposing one.
 template <typename T, bool kGatherA, bool kDense>
-void wgrad(const char* name, const WgradArgs& a, int groups, hipStream_t s) {
+void wgrad(const char* name, const WgradArgs& a, int groups, const void* zero, hipStream_t s) {
+  if (std::is_same<T, bf16_t>::value && !kGatherA) {
+    wgrad_tr<kDense>(name, a, groups, static_cast<const bf16_t*>(zero), s);
+    return;
+  }
   const int64_t blocks = static_cast<int64_t>(groups) * (a.M / 128) * (a.N / 128);
   if (blocks <= 0) return;
   MOE_LAUNCH(name, (wgrad_kernel<T, kGatherA, kDense>), dim3(static_cast<unsigned>(blocks)),
@@ -386,6 +398,10 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   T* dAB = reinterpret_cast<T*>(W + L.dAB);
   T* dXs = reinterpret_cast<T*>(W + L.dXs);
   float* rpart = reinterpret_cast<float*>(W + L.rpart);
+  // Zero row the bf16 weight-gradient loads read past a group's end.
+  const void* zero_row = W + L.zero;
+  if (std::is_same<T, bf16_t>::value)
+    zero(reinterpret_cast<float*>(W + L.zero), kTrZeroBytes / 4, s);
   const int64_t row_blocks = (T_ + kRowThreads / 64 - 1) / (kRowThreads / 64);
 
   // a11: combine backward and per-slot router gradient
@@ -416,12 +432,19 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     a.nsplit = d;
     a.ldc = d;
     a.c_group_stride = static_cast<int64_t>(h) * d;
-    wgrad<T, false, false>("bwd_wgrad_down", a, E, s);
+    wgrad<T, false, false>("bwd_wgrad_down", a, E, zero_row, s);
     WgradArgs b{};
     b.a = x;
     b.lda = d;
     b.perm = r.perm;
     b.topk = k;
+    if (std::is_same<T, bf16_t>::value) {
+      // dY is dead once dW_down is out: it takes the token rows in expert order.
+      MOE_LAUNCH("bwd_sort_rows", sort_rows_kernel<T>, dim3(sort_rows_blocks(S)),
+                 dim3(kSortThreads), 0, s, static_cast<const T*>(x), r.perm, k, S, d, dY);
+      b.a = dY;
+      b.perm = nullptr;
+    }
     b.b = dAB;
     b.ldb = 2 * static_cast<int64_t>(h);
     b.M = d;
@@ -433,7 +456,8 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     b.nsplit = h;
     b.ldc = h;
     b.c_group_stride = static_cast<int64_t>(d) * h;
-    wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, s);
+    if (std::is_same<T, bf16_t>::value) wgrad<T, false, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
+    else wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
   }
   // a16: shared expert
   T* dxs = nullptr;
@@ -483,7 +507,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     c.nsplit = d;
     c.ldc = d;
     c.c_group_stride = static_cast<int64_t>(hs) * d;
-    wgrad<T, false, true>("bwd_shared_wgrad_down", c, L.ks_sd, s);
+    wgrad<T, false, true>("bwd_shared_wgrad_down", c, L.ks_sd, zero_row, s);
     MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p1,
                L.ks_sd, static_cast<int64_t>(hs), d, d, static_cast<int64_t>(d), g.ws_down,
                static_cast<float*>(nullptr));
@@ -501,7 +525,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     e.nsplit = 2 * hs;
     e.ldc = 2 * static_cast<int64_t>(hs);
     e.c_group_stride = static_cast<int64_t>(d) * 2 * hs;
-    wgrad<T, false, true>("bwd_shared_wgrad_gate_up", e, L.ks_sgu, s);
+    wgrad<T, false, true>("bwd_shared_wgrad_gate_up", e, L.ks_sgu, zero_row, s);
     MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p2,
                L.ks_sgu, static_cast<int64_t>(d), 2 * hs, hs, static_cast<int64_t>(hs), g.ws_gate,
                g.ws_up);

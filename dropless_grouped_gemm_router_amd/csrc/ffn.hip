@@ -12,6 +12,7 @@
 // 32-column MFMA tile carries matching gate and up columns and the SwiGLU
 // epilogue needs no data exchange.
 #include "gemm_launch.h"
+#include "sort_rows.h"
 
 namespace moe {
 
@@ -76,21 +77,6 @@ void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc
 
 
 
-// Dispatch "sorted": token rows copied into expert order before the
-// gate/up GEMM, x_sorted[j] = x[perm[j] / k]. One wave per row, 16-byte
-// pieces.
-template <typename T>
-__global__ __launch_bounds__(256) void sort_rows_kernel(const T* __restrict__ x,
-                                                        const int32_t* __restrict__ perm, int k,
-                                                        int64_t S, int d, T* __restrict__ xs) {
-  constexpr int V = 16 / static_cast<int>(sizeof(T));
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (j >= S) return;
-  const int64_t t = perm[j] / k;
-  for (int c = (threadIdx.x & 63) * V; c < d; c += 64 * V)
-    *reinterpret_cast<u32x4*>(xs + j * d + c) = *reinterpret_cast<const u32x4*>(x + t * d + c);
-}
-
 // Fused gather-sum: the shared down GEMM writes out[t] = sum_i w y + shared.
 struct FuseCombine {
   void* out;
@@ -106,7 +92,7 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   const int64_t S = p.tokens * p.top_k;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
   if (x_sorted)
-    MOE_LAUNCH("sort_rows", sort_rows_kernel<T>, dim3(static_cast<unsigned>((S + 3) / 4)), dim3(256),
+    MOE_LAUNCH("sort_rows", sort_rows_kernel<T>, dim3(sort_rows_blocks(S)), dim3(kSortThreads),
                0, s, static_cast<const T*>(x), r.perm, p.top_k, S, p.d_model,
                static_cast<T*>(x_sorted));
   GemmArgs a{};

@@ -221,6 +221,45 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p,
         wt[ii] = ii < p.gk ? p.gw[orow * p.gk + ii] : 0.0f;
       }
     }
+    if (kEpi == kEpiSwigluBwd) {
+      // The saved pre-activations of JB MFMA tiles are all loaded before
+      // any result is stored: interleaved, each load would wait behind the
+      // previous stores (they may alias as far as the compiler knows),
+      // one memory round trip per four columns.
+      constexpr int JB = WM_SUB >= 4 ? 1 : (WN_SUB > 2 ? 2 : WN_SUB);
+      const T* sa = static_cast<const T*>(p.sa);
+      const T* sb = static_cast<const T*>(p.sb);
+#pragma unroll
+      for (int jb = 0; jb < WN_SUB; jb += JB) {
+        float a[JB][4][4], b[JB][4][4];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int n = nt * BN + wn * WN_SUB * 32 + (jb + jj) * 32 + 8 * rr + 4 * g;
+            load4(sa + orow * p.lds + n, a[jj][rr]);
+            load4(sb + orow * p.lds + n, b[jj][rr]);
+          }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int n = nt * BN + wn * WN_SUB * 32 + (jb + jj) * 32 + 8 * rr + 4 * g;
+            float da[4], db[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float dh = acc[i][jb + jj][4 * rr + q];
+              const float av = a[jj][rr][q], bv = b[jj][rr][q];
+              const float sg = sigmoid_f(av);
+              da[q] = dh * bv * sg * (1.0f + av * (1.0f - sg));
+              db[q] = dh * av * sg;
+            }
+            store4(c + orow * p.ldc + n, da[0], da[1], da[2], da[3]);
+            store4(c + orow * p.ldc + p.hsplit + n, db[0], db[1], db[2], db[3]);
+          }
+      }
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < WN_SUB; ++j) {
       const int n0 = nt * BN + wn * WN_SUB * 32 + j * 32;
@@ -237,25 +276,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p,
           const int n = n0 + 8 * rr + 4 * g;
           store4(c + orow * p.ldc + n, acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1],
                  acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]);
-        }
-      } else if (kEpi == kEpiSwigluBwd) {
-        const T* sa = static_cast<const T*>(p.sa);
-        const T* sb = static_cast<const T*>(p.sb);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int n = n0 + 8 * rr + 4 * g;
-          float a[4], b[4], da[4], db[4];
-          load4(sa + orow * p.lds + n, a);
-          load4(sb + orow * p.lds + n, b);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float dh = acc[i][j][4 * rr + q];
-            const float sg = sigmoid_f(a[q]);
-            da[q] = dh * b[q] * sg * (1.0f + a[q] * (1.0f - sg));
-            db[q] = dh * a[q] * sg;
-          }
-          store4(c + orow * p.ldc + n, da[0], da[1], da[2], da[3]);
-          store4(c + orow * p.ldc + p.hsplit + n, db[0], db[1], db[2], db[3]);
         }
       } else {
         // Packed columns [n0, n0+16) are gate columns n0/2 + [0,16) and

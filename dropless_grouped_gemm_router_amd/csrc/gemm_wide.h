@@ -161,11 +161,19 @@ __device__ __forceinline__ void wide_park(char* region, int row, int byte, float
 // 64 bf16 columns, for rows r < rows.
 __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int64_t ld, int rows,
                                            int lane) {
+  // All eight LDS reads first (always in bounds), then the row-guarded
+  // stores: a guarded read-store pair per row would wait out each read.
+  const int c = lane & 7;
+  u32x4 v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int r = k * 8 + (lane >> 3), c = lane & 7;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
-    if (r < rows) *reinterpret_cast<u32x4*>(dst + r * ld + c * 8) = v;
+    const int r = k * 8 + (lane >> 3);
+    v[k] = *reinterpret_cast<const u32x4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int r = k * 8 + (lane >> 3);
+    if (r < rows) *reinterpret_cast<u32x4*>(dst + r * ld + c * 8) = v[k];
   }
 }
 
