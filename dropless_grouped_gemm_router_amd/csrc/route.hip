@@ -212,10 +212,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const T* __restric
 // once per CU. Same lane layout and the same fp32 chain per logit as
 // route_kernel; the next 8 token values of each row are loaded while the
 // current 8 are multiplied in.
-constexpr int kResidentThreads = 1024;
+constexpr int kResidentThreads = 1024;  // default workgroup size of the resident kernel
 
-template <typename T, int L, int P, int R>
-__global__ __launch_bounds__(kResidentThreads) void route_resident_kernel(
+template <typename T, int L, int P, int R, int NT>
+__global__ __launch_bounds__(NT) void route_resident_kernel(
     const T* __restrict__ x, const float* __restrict__ wr, int64_t ntok, int d, int E, int k,
     int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   constexpr int EPAD = L * P;
@@ -223,13 +223,13 @@ __global__ __launch_bounds__(kResidentThreads) void route_resident_kernel(
   constexpr int kPerPiece = 16 / static_cast<int>(sizeof(T));
   extern __shared__ __attribute__((aligned(16))) float w_res[];  // [EPAD][d + kRoutePad]
   const int stride = d + kRoutePad;
-  for (int i = threadIdx.x; i < d * EPAD; i += kResidentThreads) {
+  for (int i = threadIdx.x; i < d * EPAD; i += NT) {
     const int jj = i / EPAD, ee = i % EPAD;
     w_res[ee * stride + jj] = (ee < E) ? wr[static_cast<int64_t>(jj) * E + ee] : 0.0f;
   }
   __syncthreads();
 
-  constexpr int kTokPerPass = (kResidentThreads / 64) * (64 / L) * R;
+  constexpr int kTokPerPass = (NT / 64) * (64 / L) * R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int le = lane % L, grp = lane / L;
   for (int64_t base = static_cast<int64_t>(blockIdx.x) * kTokPerPass; base < ntok;
@@ -297,19 +297,19 @@ size_t resident_lds_bytes(int d) {
   return static_cast<size_t>(L) * P * (d + kRoutePad) * sizeof(float);
 }
 
-template <typename T, int L, int P, int R>
+template <typename T, int L, int P, int R, int NT = kResidentThreads>
 hipError_t launch_route_resident(const void* x, const float* wr, int64_t T_, int d, int E, int k,
                                  int32_t* idx, float* w, hipStream_t s) {
   const size_t lds = resident_lds_bytes<T, L, P, R>(d);
-  auto kern = route_resident_kernel<T, L, P, R>;
+  auto kern = route_resident_kernel<T, L, P, R, NT>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  constexpr int kTokPerPass = (kResidentThreads / 64) * (64 / L) * R;
+  constexpr int kTokPerPass = (NT / 64) * (64 / L) * R;
   const int64_t passes = (T_ + kTokPerPass - 1) / kTokPerPass;
   const int64_t blocks = passes < cu_count() ? passes : cu_count();
-  MOE_LAUNCH("route", kern, dim3(static_cast<unsigned>(blocks)), dim3(kResidentThreads), lds, s,
+  MOE_LAUNCH("route", kern, dim3(static_cast<unsigned>(blocks)), dim3(NT), lds, s,
              static_cast<const T*>(x), wr, T_, d, E, k, idx, w);
   return hipGetLastError();
 }
@@ -345,7 +345,11 @@ hipError_t launch_route_dt(const void* x, const float* wr, int64_t T_, int d, in
       if (fits(8, 2)) return launch_route_resident<T, 8, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
       return launch_route_resident<T, 8, 4, 1>(x, wr, T_, d, E, k, idx, w, s);
     }
-    if (fits(16, 4)) return launch_route_resident<T, 16, 4, 4>(x, wr, T_, d, E, k, idx, w, s);
+    // Eight experts per lane for large batches: each widened token value
+    // feeds eight FMAs instead of four (the 210 registers this takes need
+    // 512-thread workgroups; 0.238 -> 0.228 ms at 131072 tokens, E=64).
+    if (fits(16, 4))
+      return launch_route_resident<T, 8, 8, 4, 512>(x, wr, T_, d, E, k, idx, w, s);
     if (fits(16, 2)) return launch_route_resident<T, 16, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
     return launch_route_resident<T, 16, 4, 1>(x, wr, T_, d, E, k, idx, w, s);
   }

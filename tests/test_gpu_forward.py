@@ -44,6 +44,9 @@ SMALL = [
     # skewed routing (uneven expert loads, nearly empty experts)
     Problem(3000, 64, 8, 256, 128, 128, "bf16", 256, skew=0.9),
     Problem(3000, 64, 8, 256, 128, 0, "bf16", 64, skew=0.9),
+    # 64 experts and more than 65536 tokens: the router's 8-lane x 8-expert
+    # layout in 512-thread workgroups; 66000 leaves a ragged last pass
+    Problem(66000, 64, 8, 128, 64, 0, "bf16", 256),
     # capacity routing: the busier experts drop their last slots
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),
     Problem(517, 16, 4, 256, 192, 128, "fp32", 32, capacity=100),
