@@ -404,131 +404,151 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     zero(reinterpret_cast<float*>(W + L.zero), kTrZeroBytes / 4, s);
   const int64_t row_blocks = (T_ + kRowThreads / 64 - 1) / (kRowThreads / 64);
 
-  // a11: combine backward and per-slot router gradient
-  MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
-             dim3(kRowThreads), 0, s, T_, k, d, static_cast<const T*>(grad_out),
-             static_cast<const T*>(y_sorted), r.topk_w, r.inv_perm, dY, dl);
-  // a12: router weight gradient (tile partials, then a per-expert ordered sum)
-  MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
-             dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
-             r.expert_offsets, E, p.block_m, rpart);
-  MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
-             r.expert_offsets, E, p.block_m, d, g.w_router);
-  // a13 + a15: dgrad GEMMs
-  const void* sab = SV + F.sv_ab;
-  routed_dgrad<T>(p, w, r, sab, dY, dAB, dXs, s);
-  // a14: per-expert weight gradients, K = the expert's rows
-  {
-    WgradArgs a{};
-    a.a = SV + F.sv_h;
-    a.lda = h;
-    a.b = dY;
-    a.ldb = d;
-    a.M = h;
-    a.N = d;
-    a.row_offsets = r.expert_offsets;
-    a.cap = p.capacity;
-    a.c = g.w_down;
-    a.nsplit = d;
-    a.ldc = d;
-    a.c_group_stride = static_cast<int64_t>(h) * d;
-    wgrad<T, false, false>("bwd_wgrad_down", a, E, zero_row, s);
-    WgradArgs b{};
-    b.a = x;
-    b.lda = d;
-    b.perm = r.perm;
-    b.topk = k;
-    if (std::is_same<T, bf16_t>::value) {
-      // dY is dead once dW_down is out: it takes the token rows in expert order.
-      MOE_LAUNCH("bwd_sort_rows", sort_rows_kernel<T>, dim3(sort_rows_blocks(S)),
-                 dim3(kSortThreads), 0, s, static_cast<const T*>(x), r.perm, k, S, d, dY);
-      b.a = dY;
-      b.perm = nullptr;
-    }
-    b.b = dAB;
-    b.ldb = 2 * static_cast<int64_t>(h);
-    b.M = d;
-    b.N = 2 * h;
-    b.row_offsets = r.expert_offsets;
-    b.cap = p.capacity;
-    b.c = g.w_gate;
-    b.c2 = g.w_up;
-    b.nsplit = h;
-    b.ldc = h;
-    b.c_group_stride = static_cast<int64_t>(d) * h;
-    if (std::is_same<T, bf16_t>::value) wgrad<T, false, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
-    else wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
-  }
-  // a16: shared expert
   T* dxs = nullptr;
-  if (hs > 0) {
-    T* dABs = reinterpret_cast<T*>(W + L.dABs);
-    dxs = reinterpret_cast<T*>(W + L.dxs);
-    const T* ssab = reinterpret_cast<const T*>(SV + F.sv_sab);
-    GemmArgs a{};
-    a.a = grad_out;
-    a.lda = d;
-    a.b = w.ws_down;  // [hs][d]
-    a.N = hs;
-    a.K = d;
-    a.M = T_;
-    a.c = dABs;
-    a.ldc = 2 * static_cast<int64_t>(hs);
-    a.hsplit = hs;
-    a.sa = const_cast<T*>(ssab);
-    a.sb = const_cast<T*>(ssab + hs);
-    a.lds = 2 * static_cast<int64_t>(hs);
-    dense_gemm<T, kEpiSwigluBwd>("bwd_shared_down_dgrad", a, s);
-    GemmArgs b{};
-    b.a = dABs;
-    b.lda = 2 * static_cast<int64_t>(hs);
-    b.b = w.ws_gate;  // [d][hs]
-    b.ldb = hs;
-    b.b2 = w.ws_up;
-    b.ksplit = hs;
-    b.N = d;
-    b.K = 2 * hs;
-    b.M = T_;
-    b.c = dxs;
-    b.ldc = d;
-    dense_gemm<T, kEpiStore>("bwd_shared_gate_up_dgrad", b, s);
+  // a11-a14 (routed path) and a16 (shared expert); the shared expert needs
+  // only grad_out, the tokens and its own saved activations, so it runs on
+  // the side stream beside the routed path (each lambda's stream parameter
+  // is the `s` its launches use).
+  auto routed_bwd = [&](hipStream_t s) {
+    // a11: combine backward and per-slot router gradient
+    MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
+               dim3(kRowThreads), 0, s, T_, k, d, static_cast<const T*>(grad_out),
+               static_cast<const T*>(y_sorted), r.topk_w, r.inv_perm, dY, dl);
+    // a12: router weight gradient (tile partials, then a per-expert ordered sum)
+    MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
+               dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
+               r.expert_offsets, E, p.block_m, rpart);
+    MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
+               r.expert_offsets, E, p.block_m, d, g.w_router);
+    // a13 + a15: dgrad GEMMs
+    const void* sab = SV + F.sv_ab;
+    routed_dgrad<T>(p, w, r, sab, dY, dAB, dXs, s);
+    // a14: per-expert weight gradients, K = the expert's rows
+    {
+      WgradArgs a{};
+      a.a = SV + F.sv_h;
+      a.lda = h;
+      a.b = dY;
+      a.ldb = d;
+      a.M = h;
+      a.N = d;
+      a.row_offsets = r.expert_offsets;
+      a.cap = p.capacity;
+      a.c = g.w_down;
+      a.nsplit = d;
+      a.ldc = d;
+      a.c_group_stride = static_cast<int64_t>(h) * d;
+      wgrad<T, false, false>("bwd_wgrad_down", a, E, zero_row, s);
+      WgradArgs b{};
+      b.a = x;
+      b.lda = d;
+      b.perm = r.perm;
+      b.topk = k;
+      if (std::is_same<T, bf16_t>::value) {
+        // dY is dead once dW_down is out: it takes the token rows in expert order.
+        MOE_LAUNCH("bwd_sort_rows", sort_rows_kernel<T>, dim3(sort_rows_blocks(S)),
+                   dim3(kSortThreads), 0, s, static_cast<const T*>(x), r.perm, k, S, d, dY);
+        b.a = dY;
+        b.perm = nullptr;
+      }
+      b.b = dAB;
+      b.ldb = 2 * static_cast<int64_t>(h);
+      b.M = d;
+      b.N = 2 * h;
+      b.row_offsets = r.expert_offsets;
+      b.cap = p.capacity;
+      b.c = g.w_gate;
+      b.c2 = g.w_up;
+      b.nsplit = h;
+      b.ldc = h;
+      b.c_group_stride = static_cast<int64_t>(d) * h;
+      if (std::is_same<T, bf16_t>::value) wgrad<T, false, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
+      else wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
+    }
+  };
+  auto shared_bwd = [&](hipStream_t s) {
+    // a16: shared expert
+    if (hs > 0) {
+      T* dABs = reinterpret_cast<T*>(W + L.dABs);
+      dxs = reinterpret_cast<T*>(W + L.dxs);
+      const T* ssab = reinterpret_cast<const T*>(SV + F.sv_sab);
+      GemmArgs a{};
+      a.a = grad_out;
+      a.lda = d;
+      a.b = w.ws_down;  // [hs][d]
+      a.N = hs;
+      a.K = d;
+      a.M = T_;
+      a.c = dABs;
+      a.ldc = 2 * static_cast<int64_t>(hs);
+      a.hsplit = hs;
+      a.sa = const_cast<T*>(ssab);
+      a.sb = const_cast<T*>(ssab + hs);
+      a.lds = 2 * static_cast<int64_t>(hs);
+      dense_gemm<T, kEpiSwigluBwd>("bwd_shared_down_dgrad", a, s);
+      GemmArgs b{};
+      b.a = dABs;
+      b.lda = 2 * static_cast<int64_t>(hs);
+      b.b = w.ws_gate;  // [d][hs]
+      b.ldb = hs;
+      b.b2 = w.ws_up;
+      b.ksplit = hs;
+      b.N = d;
+      b.K = 2 * hs;
+      b.M = T_;
+      b.c = dxs;
+      b.ldc = d;
+      dense_gemm<T, kEpiStore>("bwd_shared_gate_up_dgrad", b, s);
 
-    float* p1 = reinterpret_cast<float*>(W + L.part_sd);
-    WgradArgs c{};
-    c.a = SV + F.sv_sh;
-    c.lda = hs;
-    c.b = grad_out;
-    c.ldb = d;
-    c.M = hs;
-    c.N = d;
-    c.rows_total = T_;
-    c.splits = L.ks_sd;
-    c.c = p1;
-    c.nsplit = d;
-    c.ldc = d;
-    c.c_group_stride = static_cast<int64_t>(hs) * d;
-    wgrad<T, false, true>("bwd_shared_wgrad_down", c, L.ks_sd, zero_row, s);
-    MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p1,
-               L.ks_sd, static_cast<int64_t>(hs), d, d, static_cast<int64_t>(d), g.ws_down,
-               static_cast<float*>(nullptr));
-    float* p2 = reinterpret_cast<float*>(W + L.part_sgu);
-    WgradArgs e{};
-    e.a = x;
-    e.lda = d;
-    e.b = dABs;
-    e.ldb = 2 * static_cast<int64_t>(hs);
-    e.M = d;
-    e.N = 2 * hs;
-    e.rows_total = T_;
-    e.splits = L.ks_sgu;
-    e.c = p2;
-    e.nsplit = 2 * hs;
-    e.ldc = 2 * static_cast<int64_t>(hs);
-    e.c_group_stride = static_cast<int64_t>(d) * 2 * hs;
-    wgrad<T, false, true>("bwd_shared_wgrad_gate_up", e, L.ks_sgu, zero_row, s);
-    MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p2,
-               L.ks_sgu, static_cast<int64_t>(d), 2 * hs, hs, static_cast<int64_t>(hs), g.ws_gate,
-               g.ws_up);
+      float* p1 = reinterpret_cast<float*>(W + L.part_sd);
+      WgradArgs c{};
+      c.a = SV + F.sv_sh;
+      c.lda = hs;
+      c.b = grad_out;
+      c.ldb = d;
+      c.M = hs;
+      c.N = d;
+      c.rows_total = T_;
+      c.splits = L.ks_sd;
+      c.c = p1;
+      c.nsplit = d;
+      c.ldc = d;
+      c.c_group_stride = static_cast<int64_t>(hs) * d;
+      wgrad<T, false, true>("bwd_shared_wgrad_down", c, L.ks_sd, zero_row, s);
+      MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p1,
+                 L.ks_sd, static_cast<int64_t>(hs), d, d, static_cast<int64_t>(d), g.ws_down,
+                 static_cast<float*>(nullptr));
+      float* p2 = reinterpret_cast<float*>(W + L.part_sgu);
+      WgradArgs e{};
+      e.a = x;
+      e.lda = d;
+      e.b = dABs;
+      e.ldb = 2 * static_cast<int64_t>(hs);
+      e.M = d;
+      e.N = 2 * hs;
+      e.rows_total = T_;
+      e.splits = L.ks_sgu;
+      e.c = p2;
+      e.nsplit = 2 * hs;
+      e.ldc = 2 * static_cast<int64_t>(hs);
+      e.c_group_stride = static_cast<int64_t>(d) * 2 * hs;
+      wgrad<T, false, true>("bwd_shared_wgrad_gate_up", e, L.ks_sgu, zero_row, s);
+      MOE_LAUNCH("bwd_split_reduce", split_reduce_kernel, dim3(2048), dim3(kRowThreads), 0, s, p2,
+                 L.ks_sgu, static_cast<int64_t>(d), 2 * hs, hs, static_cast<int64_t>(hs), g.ws_gate,
+                 g.ws_up);
+    }
+  };
+  if (hs > 0) {
+    SideFork fork;
+    hipError_t e = fork.fork(s);
+    if (e != hipSuccess) return e;
+    shared_bwd(fork.side());
+    routed_bwd(s);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = fork.join(s);
+    if (e != hipSuccess) return e;
+  } else {
+    routed_bwd(s);
   }
   // dx: gather-sum of the routed input gradients plus the router and shared terms
   float* wrT = reinterpret_cast<float*>(W + L.wrT);

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "moe.h"
 
 namespace moe {
@@ -100,6 +102,26 @@ int persistent_slots(const void* kernel, int threads);
 // Compute units of the current device.
 int cu_count();
 
+// Fork onto and join back from the current device's side stream (default
+// priority, non-blocking; created on first use and kept for the process).
+// The object holds a process-wide lock from construction to destruction, so
+// concurrent callers never interleave records and waits on the shared fork
+// and join events; work enqueued on side() between fork(s) and join(s) runs
+// beside s, after everything enqueued on s before the fork, and s waits for
+// it from the join on.
+class SideFork {
+ public:
+  SideFork();
+  hipError_t fork(hipStream_t s);
+  hipError_t join(hipStream_t s);
+  hipStream_t side() const { return side_; }
+
+ private:
+  std::lock_guard<std::mutex> lock_;
+  int dev_ = 0;
+  hipStream_t side_ = nullptr;
+};
+
 // Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).
 void trace_push(hipStream_t s, const char* name);
 void trace_pop(hipStream_t s);
@@ -139,11 +161,11 @@ hipError_t launch_ffn_fwd(const moe_problem& p, const void* x, const moe_weights
                           const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
                           void* ws, hipStream_t s);
 
-// Whole forward (moe_forward): workspace offsets (bytes) of the staged
-// shared-expert output and of the expert-ordered token copy, after the
-// permute/FFN area at offset 0.
+// Whole forward (moe_forward): workspace offsets (bytes) of the permute
+// scratch, the staged shared-expert output and the expert-ordered token
+// copy, after the FFN area at offset 0.
 struct ForwardLayout {
-  size_t shared_out, x_sorted, total;
+  size_t permute, shared_out, x_sorted, total;
   bool fused;  // the combine runs in the shared down GEMM's epilogue
 };
 ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training);

@@ -166,30 +166,47 @@ void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void
   }
 }
 
+// Routed part: pack the expert weights, gate/up GEMM with SwiGLU, down GEMM.
 template <typename T>
-hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
-                     const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
-                     void* ws, void* x_sorted, const FuseCombine* fuse, hipStream_t s) {
+void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
+                  const moe_routing& r, void* y_sorted, void* saved, void* ws, void* x_sorted,
+                  hipStream_t s) {
   const FfnLayout L = ffn_layout(p, saved != nullptr);
   char* W = static_cast<char*>(ws);
   char* SV = static_cast<char*>(saved);
-  const int E = p.experts, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+  const int E = p.experts, d = p.d_model, h = p.d_hidden;
   pack<T>(w.w_gate, w.w_up, W + L.gu_packed, E, d, h, true, s);
   pack<T>(w.w_down, nullptr, W + L.down_packed, E, h, d, false, s);
-  if (hs > 0) {
-    pack<T>(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true, s);
-    pack<T>(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false, s);
-  }
   T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
   routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, x_sorted, s);
-  if (hs > 0) {
-    T* hsb = saved ? reinterpret_cast<T*>(SV + L.sv_sh) : reinterpret_cast<T*>(W + L.h_shared);
-    T* ssa = saved ? reinterpret_cast<T*>(SV + L.sv_sab) : nullptr;
-    T* ssb = saved ? ssa + hs : nullptr;
-    shared_ffn<T>(p, x, W + L.sgu_packed, W + L.sdown_packed, hsb, shared_out, ssa, ssb, fuse, s);
-  }
+}
+
+// Shared part (d_shared > 0): pack its weights, its two GEMMs. It touches
+// only its own workspace and saved regions, so it may run beside the
+// routed part on another stream.
+template <typename T>
+void ffn_shared_t(const moe_problem& p, const void* x, const moe_weights& w, void* shared_out,
+                  void* saved, void* ws, const FuseCombine* fuse, hipStream_t s) {
+  const FfnLayout L = ffn_layout(p, saved != nullptr);
+  char* W = static_cast<char*>(ws);
+  char* SV = static_cast<char*>(saved);
+  const int d = p.d_model, hs = p.d_shared;
+  pack<T>(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true, s);
+  pack<T>(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false, s);
+  T* hsb = saved ? reinterpret_cast<T*>(SV + L.sv_sh) : reinterpret_cast<T*>(W + L.h_shared);
+  T* ssa = saved ? reinterpret_cast<T*>(SV + L.sv_sab) : nullptr;
+  T* ssb = saved ? ssa + hs : nullptr;
+  shared_ffn<T>(p, x, W + L.sgu_packed, W + L.sdown_packed, hsb, shared_out, ssa, ssb, fuse, s);
+}
+
+template <typename T>
+hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
+                     const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
+                     void* ws, void* x_sorted, const FuseCombine* fuse, hipStream_t s) {
+  ffn_routed_t<T>(p, x, w, r, y_sorted, saved, ws, x_sorted, s);
+  if (p.d_shared > 0) ffn_shared_t<T>(p, x, w, shared_out, saved, ws, fuse, s);
   return hipGetLastError();
 }
 
@@ -230,9 +247,11 @@ ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training) 
   const size_t T = static_cast<size_t>(p.tokens), S = T * p.top_k;
   ForwardLayout L{};
   L.fused = dispatch == MOE_DISPATCH_FUSED_GSUM && p.d_shared > 0 && p.top_k <= kCombineMaxK;
-  size_t o = permute_ws_bytes(static_cast<int64_t>(S), p.experts);
-  const size_t f = ffn_layout(p, training).total;
-  o = align_up(o > f ? o : f, 256);
+  // The permute scratch has a region of its own: the shared expert may be
+  // packing its weights while the permutation runs.
+  size_t o = align_up(ffn_layout(p, training).total, 256);
+  L.permute = o;
+  o = align_up(o + permute_ws_bytes(static_cast<int64_t>(S), p.experts), 256);
   L.shared_out = o;
   if (p.d_shared > 0 && !L.fused) o = align_up(o + T * p.d_model * es, 256);
   L.x_sorted = o;
@@ -241,24 +260,58 @@ ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training) 
   return L;
 }
 
+namespace {
+
+// route -> permute -> routed FFN on s.
+hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights& w,
+                          const moe_routing& r, void* y_sorted, void* saved, void* ws,
+                          void* x_sorted, void* permute_ws, hipStream_t s) {
+  hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
+                              r.topk_idx, r.topk_w, s);
+  if (e != hipSuccess) return e;
+  e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, p.capacity, r.topk_idx,
+                     r.expert_offsets, r.perm, r.inv_perm, r.tiles, r.num_tiles, permute_ws, s);
+  if (e != hipSuccess) return e;
+  if (p.dtype == MOE_BF16) ffn_routed_t<bf16_t>(p, x, w, r, y_sorted, saved, ws, x_sorted, s);
+  else ffn_routed_t<float>(p, x, w, r, y_sorted, saved, ws, x_sorted, s);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* saved, void* out, void* ws,
                           hipStream_t s) {
   const ForwardLayout L = forward_layout(p, dispatch, saved != nullptr);
   char* W = static_cast<char*>(ws);
-  hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
-                              r.topk_idx, r.topk_w, s);
-  if (e != hipSuccess) return e;
-  e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, p.capacity, r.topk_idx,
-                     r.expert_offsets, r.perm, r.inv_perm, r.tiles, r.num_tiles, ws, s);
-  if (e != hipSuccess) return e;
   void* shared_out = p.d_shared > 0 && !L.fused ? W + L.shared_out : nullptr;
   void* x_sorted = dispatch == MOE_DISPATCH_SORTED ? W + L.x_sorted : nullptr;
-  const FuseCombine fuse{out, y_sorted, r.topk_w, r.inv_perm};
-  const FuseCombine* fp = L.fused ? &fuse : nullptr;
-  e = p.dtype == MOE_BF16
-          ? ffn_fwd_t<bf16_t>(p, x, w, r, y_sorted, shared_out, saved, ws, x_sorted, fp, s)
-          : ffn_fwd_t<float>(p, x, w, r, y_sorted, shared_out, saved, ws, x_sorted, fp, s);
+  const bool bf = p.dtype == MOE_BF16;
+  // Unfused, the shared expert depends on nothing but the tokens and its
+  // weights: it runs on the side stream beside route, permute and the routed
+  // FFN, and the combine waits for it.
+  if (p.d_shared > 0 && !L.fused) {
+    SideFork fork;
+    hipError_t e = fork.fork(s);
+    if (e != hipSuccess) return e;
+    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
+    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
+    e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = fork.join(s);
+    if (e != hipSuccess) return e;
+    return launch_combine(p.dtype, p.tokens, p.top_k, p.d_model, y_sorted, r.topk_w, r.inv_perm,
+                          shared_out, out, s);
+  }
+  hipError_t e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s);
+  if (e != hipSuccess) return e;
+  if (p.d_shared > 0) {
+    // fused: the shared down GEMM's epilogue reads the routed outputs
+    const FuseCombine fuse{out, y_sorted, r.topk_w, r.inv_perm};
+    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, L.fused ? &fuse : nullptr, s);
+    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, L.fused ? &fuse : nullptr, s);
+  }
+  e = hipGetLastError();
   if (e != hipSuccess || L.fused) return e;
   return launch_combine(p.dtype, p.tokens, p.top_k, p.d_model, y_sorted, r.topk_w, r.inv_perm,
                         shared_out, out, s);

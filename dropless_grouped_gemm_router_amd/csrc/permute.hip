@@ -71,9 +71,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   // together, and kept in registers for the write-back.
   constexpr int kScanRegs = 16;
   const bool in_regs = chunk <= kScanRegs;
+  // A whole chunk of kScanRegs entries (64 bytes, 16-byte aligned since b0
+  // is a multiple of chunk) moves as four 16-byte accesses.
+  const bool whole = chunk == kScanRegs && b1 - b0 == kScanRegs;
   int32_t vals[kScanRegs];
   int32_t local = 0;
-  if (in_regs) {
+  if (whole) {
+#pragma unroll
+    for (int q = 0; q < kScanRegs / 4; ++q) {
+      const int4 v = *reinterpret_cast<const int4*>(blk_counts + b0 + 4 * q);
+      vals[4 * q] = v.x; vals[4 * q + 1] = v.y; vals[4 * q + 2] = v.z; vals[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int q = 0; q < kScanRegs; ++q) local += vals[q];
+  } else if (in_regs) {
 #pragma unroll
     for (int q = 0; q < kScanRegs; ++q) {
       const int64_t i = b0 + q;
@@ -104,7 +115,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   }
   __syncthreads();
   int32_t run = wsum[wave] + incl - local;
-  if (in_regs) {
+  if (whole) {
+    int32_t ex[kScanRegs];
+#pragma unroll
+    for (int q = 0; q < kScanRegs; ++q) {
+      const int64_t i = b0 + q;
+      ex[q] = run;
+      if (i % nblk == 0) off[i / nblk] = run;  // block 0 of expert i / nblk
+      run += vals[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kScanRegs / 4; ++q)
+      *reinterpret_cast<int4*>(blk_counts + b0 + 4 * q) =
+          make_int4(ex[4 * q], ex[4 * q + 1], ex[4 * q + 2], ex[4 * q + 3]);
+  } else if (in_regs) {
 #pragma unroll
     for (int q = 0; q < kScanRegs; ++q) {
       const int64_t i = b0 + q;

@@ -1,4 +1,5 @@
-// Resident-workgroup counts for persistent kernels.
+// Resident-workgroup counts for persistent kernels, and the side stream that
+// runs the shared expert beside the routed path.
 #include <hip/hip_runtime.h>
 
 #include <map>
@@ -44,6 +45,40 @@ int cu_count() {
     cus = 256;
   cache[dev] = cus;
   return cus;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxDevices];
+hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices];
+}  // namespace
+
+SideFork::SideFork() : lock_(g_side_mu) {}
+
+hipError_t SideFork::fork(hipStream_t s) {
+  hipError_t e = hipGetDevice(&dev_);
+  if (e == hipSuccess && (dev_ < 0 || dev_ >= kMaxDevices)) e = hipErrorInvalidDevice;
+  if (e != hipSuccess) return e;
+  if (!g_side[dev_]) {
+    e = hipStreamCreateWithFlags(&g_side[dev_], hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_fork[dev_], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_join[dev_], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      g_side[dev_] = nullptr;
+      return e;
+    }
+  }
+  e = hipEventRecord(g_fork[dev_], s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(g_side[dev_], g_fork[dev_], 0);
+  if (e == hipSuccess) side_ = g_side[dev_];
+  return e;
+}
+
+hipError_t SideFork::join(hipStream_t s) {
+  hipError_t e = hipEventRecord(g_join[dev_], side_);
+  if (e == hipSuccess) e = hipStreamWaitEvent(s, g_join[dev_], 0);
+  return e;
 }
 
 }  // namespace moe
