@@ -348,6 +348,8 @@ def main():
                     help="tokens the CPU oracle runs on (about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of one forward step captured in a HIP graph")
     ap.add_argument("--maxtok", action="store_true",
                     help="largest train step that fits (E8 top-2 d512 h1024 bf16) and peak memory")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -413,8 +415,20 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    timed = step
+    if args.graph:
+        # One step captured in a HIP graph (the side-stream fork and join
+        # included), replayed as the timed step.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        timed = graph.replay
+        for _ in range(args.warmup):
+            timed()
+        torch.cuda.synchronize()
     print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
-    ms = time_steps(step, args.steps, 0)
+    ms = time_steps(timed, args.steps, 0)
     # Per-kernel times: libmoe's HIP events bracket every launch. In the
     # timed steps the shared expert runs beside the routed path on a second
     # stream, so kernel durations there include time shared with other
@@ -463,7 +477,8 @@ def main():
         "config": {"workload": name, "tokens": p.tokens, "experts": p.experts, "top_k": p.top_k,
                    "d_model": p.d_model, "d_hidden": p.d_hidden, "d_shared": p.d_shared,
                    "block_m": p.block_m, "skew": p.skew, "dispatch": args.dispatch,
-                   "routing": "capacity" if p.capacity else "dropless", "capacity": p.capacity},
+                   "routing": "capacity" if p.capacity else "dropless", "capacity": p.capacity,
+                   "hip_graph": bool(args.graph)},
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
         "roofline": roof,
