@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kRowThreads) void fill_zero_kernel(float* __restric
 }
 
 struct BwdLayout {
-  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, total;
+  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, tiles256, total;
   int ks_sd, ks_sgu;
 };
 
@@ -313,6 +313,7 @@ BwdLayout bwd_layout(const moe_problem& p) {
   L.part_sgu = o; o = align_up(o + static_cast<size_t>(L.ks_sgu) * d * 2 * hs * 4, 256);
   L.wrT = o;      o = align_up(o + static_cast<size_t>(p.experts) * d * 4, 256);
   L.zero = o;     o = align_up(o + kTrZeroBytes, 256);
+  L.tiles256 = o; o = align_up(o + retile_bytes(static_cast<int64_t>(S), p.experts), 256);
   L.total = o;
   return L;
 }
@@ -343,7 +344,8 @@ void wgrad(const char* name, const WgradArgs& a, int groups, const void* zero, h
 
 template <typename T>
 void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
-                  const void* saved_ab, const void* dY, void* dAB, void* dXs, hipStream_t s) {
+                  const void* saved_ab, const void* dY, void* dAB, void* dXs, void* tiles256,
+                  hipStream_t s) {
   const int64_t S = p.tokens * p.top_k;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
   const int d = p.d_model, h = p.d_hidden;
@@ -379,7 +381,17 @@ void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing&
   b.num_tiles = r.num_tiles;
   b.c = dXs;
   b.ldc = d;
-  grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, p.block_m, max_tiles, s);
+  if (retile_rows(p) && wide_fits<T>(b)) {
+    // 256-row tiles on the wide engine (K = 2h, N = d_model)
+    int32_t* t256 = static_cast<int32_t*>(tiles256);
+    const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
+    launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
+    b.tiles = t256 + 4;
+    b.num_tiles = t256;
+    grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, kRetileBm, mt256, s);
+  } else {
+    grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, p.block_m, max_tiles, s);
+  }
 }
 
 template <typename T>
@@ -422,7 +434,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
                r.expert_offsets, E, p.block_m, d, g.w_router);
     // a13 + a15: dgrad GEMMs
     const void* sab = SV + F.sv_ab;
-    routed_dgrad<T>(p, w, r, sab, dY, dAB, dXs, s);
+    routed_dgrad<T>(p, w, r, sab, dY, dAB, dXs, W + L.tiles256, s);
     // a14: per-expert weight gradients, K = the expert's rows
     {
       WgradArgs a{};

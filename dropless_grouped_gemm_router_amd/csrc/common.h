@@ -145,13 +145,31 @@ hipError_t launch_permute(int64_t T, int k, int E, int bm, int cap, const int32_
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tiles,
                           int32_t* num_tiles, void* ws, hipStream_t s);
 
+// 256-row tile list for the GEMMs that run faster on the wide engine than
+// on the caller's block_m (see retile_rows), from the expert offsets.
+hipError_t launch_retile(const int32_t* offsets, int E, int bm2, int cap, int32_t* tiles,
+                         int32_t* num_tiles, hipStream_t s);
+constexpr int kRetileBm = 256;
+// Bytes of a retiled list for S token-slots and E experts (tiles + count).
+inline size_t retile_bytes(int64_t S, int E) {
+  return static_cast<size_t>((S + kRetileBm - 1) / kRetileBm + E) * 12 + 16;
+}
+// Whether a bf16 grouped GEMM over block_m-row tiles takes a 256-row list
+// instead: the caller's tiles are narrower and experts average at least 512
+// rows (fewer padded rows than that make the wider tiles a loss).
+inline bool retile_rows(const moe_problem& p) {
+  return p.dtype == MOE_BF16 && p.block_m < kRetileBm &&
+         p.tokens * p.top_k >= static_cast<int64_t>(512) * p.experts;
+}
+
 hipError_t launch_combine(int dtype, int64_t T, int k, int d, const void* y_sorted,
                           const float* topk_w, const int32_t* inv_perm, const void* shared_out,
                           void* out, hipStream_t s);
 
 struct FfnLayout {
-  // workspace offsets (bytes) of the packed weights and activations
-  size_t gu_packed, down_packed, sgu_packed, sdown_packed, h_sorted, h_shared, total;
+  // workspace offsets (bytes) of the packed weights and activations, and of
+  // the 256-row tile list (retile_rows)
+  size_t gu_packed, down_packed, sgu_packed, sdown_packed, h_sorted, h_shared, tiles256, total;
   // saved-buffer offsets (bytes)
   size_t sv_ab, sv_h, sv_sab, sv_sh, sv_total;
 };

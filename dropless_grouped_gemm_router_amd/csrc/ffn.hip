@@ -88,7 +88,7 @@ struct FuseCombine {
 template <typename T>
 void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const void* gu,
                 const void* dn, void* h_sorted, void* y_sorted, void* sa, void* sb, void* x_sorted,
-                hipStream_t s) {
+                void* tiles256, hipStream_t s) {
   const int64_t S = p.tokens * p.top_k;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
   if (x_sorted)
@@ -125,7 +125,18 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   b.num_tiles = r.num_tiles;
   b.c = y_sorted;
   b.ldc = p.d_model;
-  grouped_gemm<T, false, kEpiStore>("gemm_down", b, p.block_m, max_tiles, s);
+  if (retile_rows(p) && wide_fits<T>(b)) {
+    // 256-row tiles on the wide engine for the down GEMM (its output stores
+    // dominate, and the wide engine parks them as whole row pieces)
+    int32_t* t256 = static_cast<int32_t*>(tiles256);
+    const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
+    launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
+    b.tiles = t256 + 4;
+    b.num_tiles = t256;
+    grouped_gemm<T, false, kEpiStore>("gemm_down", b, kRetileBm, mt256, s);
+  } else {
+    grouped_gemm<T, false, kEpiStore>("gemm_down", b, p.block_m, max_tiles, s);
+  }
 }
 
 template <typename T>
@@ -180,7 +191,8 @@ void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
   T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
-  routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, x_sorted, s);
+  routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, x_sorted,
+                W + L.tiles256, s);
 }
 
 // Shared part (d_shared > 0): pack its weights, its two GEMMs. It touches
@@ -224,6 +236,7 @@ FfnLayout ffn_layout(const moe_problem& p, bool training) {
   L.sdown_packed = o; o = align_up(o + d * hs * es, 256);
   L.h_sorted = o;     o = align_up(o + (training ? 0 : S * h * es), 256);
   L.h_shared = o;     o = align_up(o + (training ? 0 : T * hs * es), 256);
+  L.tiles256 = o;     o = align_up(o + retile_bytes(static_cast<int64_t>(S), p.experts), 256);
   L.total = o;
   size_t v = 0;
   L.sv_ab = v;  v = align_up(v + S * 2 * h * es, 256);

@@ -244,7 +244,49 @@ __global__ __launch_bounds__(kPermThreads) void scatter_kernel(const int32_t* __
   }
 }
 
+// A tile list with another row count bm2 from the expert offsets (the same
+// definition as the scan's list: experts ascending, each expert's kept rows
+// in pieces of bm2, the last one partial). One workgroup.
+__global__ __launch_bounds__(kScanThreads) void retile_kernel(const int32_t* __restrict__ offsets,
+                                                              int E, int bm2, int cap,
+                                                              int32_t* __restrict__ tiles,
+                                                              int32_t* __restrict__ num_tiles) {
+  __shared__ int32_t tile_off[kMaxE + 1];
+  __shared__ int32_t kept[kMaxE];
+  if (threadIdx.x < E) kept[threadIdx.x] = kept_rows(offsets[threadIdx.x + 1] - offsets[threadIdx.x], cap);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t nt = 0;
+    for (int e = 0; e < E; ++e) {
+      tile_off[e] = nt;
+      nt += (kept[e] + bm2 - 1) / bm2;
+    }
+    tile_off[E] = nt;
+    *num_tiles = nt;
+  }
+  __syncthreads();
+  const int32_t nt = tile_off[E];
+  for (int32_t n = threadIdx.x; n < nt; n += kScanThreads) {
+    int lo = 0, hi = E - 1;  // last e with tile_off[e] <= n
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tile_off[mid] <= n) lo = mid; else hi = mid - 1;
+    }
+    const int32_t r = (n - tile_off[lo]) * bm2;
+    tiles[3 * n + 0] = lo;
+    tiles[3 * n + 1] = offsets[lo] + r;
+    tiles[3 * n + 2] = min(bm2, kept[lo] - r);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_retile(const int32_t* offsets, int E, int bm2, int cap, int32_t* tiles,
+                         int32_t* num_tiles, hipStream_t s) {
+  MOE_LAUNCH("retile", retile_kernel, dim3(1), dim3(kScanThreads), 0, s, offsets, E, bm2, cap,
+             tiles, num_tiles);
+  return hipGetLastError();
+}
 
 size_t permute_ws_bytes(int64_t S, int E) {
   const int64_t nblk = (S + kSlotsPerBlock - 1) / kSlotsPerBlock;

@@ -51,6 +51,10 @@ SMALL = [
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256),
     Problem(700, 4, 2, 256, 256, 128, "fp32", 256),
     Problem(2000, 64, 8, 256, 128, 128, "bf16", 128, skew=0.9),
+    # experts averaging >= 512 rows at block_m 128: the gate/up dgrad runs on
+    # a 256-row tile list derived from the offsets (capacity-clipped too)
+    Problem(20000, 8, 2, 256, 128, 128, "bf16", 128),
+    Problem(20000, 8, 2, 256, 128, 0, "bf16", 64, capacity=4000),
     # capacity routing: dropped slots give no expert gradient but still a
     # router gradient
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),

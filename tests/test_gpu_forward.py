@@ -47,6 +47,10 @@ SMALL = [
     # 64 experts and more than 65536 tokens: the router's 8-lane x 8-expert
     # layout in 512-thread workgroups; 66000 leaves a ragged last pass
     Problem(66000, 64, 8, 128, 64, 0, "bf16", 256),
+    # experts averaging >= 512 rows at block_m < 256: the down GEMM runs on
+    # a 256-row tile list derived from the offsets (capacity-clipped too)
+    Problem(20000, 8, 2, 256, 128, 0, "bf16", 64),
+    Problem(20000, 8, 2, 256, 128, 128, "bf16", 128, capacity=4000),
     # capacity routing: the busier experts drop their last slots
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),
     Problem(517, 16, 4, 256, 192, 128, "fp32", 32, capacity=100),
