@@ -175,10 +175,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const T* __restric
   for (int j0 = 0; j0 < d; j0 += kRouteChunk) {
     const int jn = min(kRouteChunk, d - j0);
     __syncthreads();
-    // Stage W[j0 .. j0+jn)[0 .. E) transposed to [e][j].
-    for (int i = threadIdx.x; i < jn * EPAD; i += kRouteThreads) {
-      const int jj = i / EPAD, ee = i % EPAD;
-      w_lds[ee * kStride + jj] = (ee < E) ? wr[static_cast<int64_t>(j0 + jj) * E + ee] : 0.0f;
+    // Stage W[j0 .. j0+jn)[0 .. E) transposed to [e][j], kFill loads in
+    // flight per thread before their LDS stores.
+    constexpr int kFill = 16;
+    const int total = jn * EPAD;
+    for (int i0 = threadIdx.x; i0 < total; i0 += kRouteThreads * kFill) {
+      float v[kFill];
+#pragma unroll
+      for (int u = 0; u < kFill; ++u) {
+        const int i = i0 + u * kRouteThreads;
+        const int jj = i / EPAD, ee = i % EPAD;
+        v[u] = (i < total && ee < E) ? wr[static_cast<int64_t>(j0 + jj) * E + ee] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kFill; ++u) {
+        const int i = i0 + u * kRouteThreads;
+        if (i < total) w_lds[(i % EPAD) * kStride + i / EPAD] = v[u];
+      }
     }
     __syncthreads();
     for (int jj = 0; jj < jn; jj += 8) {
@@ -223,11 +236,29 @@ __global__ __launch_bounds__(NT) void route_resident_kernel(
   constexpr int kPerPiece = 16 / static_cast<int>(sizeof(T));
   extern __shared__ __attribute__((aligned(16))) float w_res[];  // [EPAD][d + kRoutePad]
   const int stride = d + kRoutePad;
-  for (int i = threadIdx.x; i < d * EPAD; i += NT) {
-    const int jj = i / EPAD, ee = i % EPAD;
-    w_res[ee * stride + jj] = (ee < E) ? wr[static_cast<int64_t>(jj) * E + ee] : 0.0f;
+  // Router fill: kFill loads in flight per thread before their LDS stores
+  // (one load at a time would cost an L2 round trip per element).
+  constexpr int kFill = 16;
+  const int total = d * EPAD;
+  for (int i0 = threadIdx.x; i0 < total; i0 += NT * kFill) {
+    float v[kFill];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int i = i0 + u * NT;
+      const int jj = i / EPAD, ee = i % EPAD;
+      v[u] = (i < total && ee < E) ? wr[static_cast<int64_t>(jj) * E + ee] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) {
+      const int i = i0 + u * NT;
+      if (i < total) w_res[(i % EPAD) * stride + i / EPAD] = v[u];
+    }
   }
   __syncthreads();
+  // Rows are d + 4 floats with d a multiple of 8: indexing whole float4s
+  // lets the reads compile to 16-byte LDS loads.
+  const float4* w4 = reinterpret_cast<const float4*>(w_res);
+  const int stride4 = stride / 4;
 
   constexpr int kTokPerPass = (NT / 64) * (64 / L) * R;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -247,39 +278,31 @@ __global__ __launch_bounds__(NT) void route_resident_kernel(
     for (int q = 0; q < P; ++q)
 #pragma unroll
       for (int r = 0; r < R; ++r) acc[q][r] = 0.0f;
-    u32x4 xn[R][XN];
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int n = 0; n < XN; ++n) xn[r][n] = *reinterpret_cast<const u32x4*>(xrow[r] + n * kPerPiece);
 
-    for (int jj = 0; jj < d; jj += 8) {
-      u32x4 xc[R][XN];
+    // Token values 8 at a time, the next 8 loaded while the current ones are
+    // multiplied in (two register sets used alternately, so nothing is
+    // copied between steps).
+    auto load = [&](u32x4 (&dst)[R][XN], int j) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int n = 0; n < XN; ++n) xc[r][n] = xn[r][n];
-      if (jj + 8 < d) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int n = 0; n < XN; ++n)
-            xn[r][n] = *reinterpret_cast<const u32x4*>(xrow[r] + jj + 8 + n * kPerPiece);
-      }
+        for (int n = 0; n < XN; ++n)
+          dst[r][n] = *reinterpret_cast<const u32x4*>(xrow[r] + j + n * kPerPiece);
+    };
+    auto step = [&](const u32x4 (&cur)[R][XN], int j) {
       // Router values four j at a time; each logit still takes j ascending.
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         float wv[P][4];
 #pragma unroll
         for (int q = 0; q < P; ++q) {
-          const float4 w4 =
-              *reinterpret_cast<const float4*>(w_res + (le + q * L) * stride + jj + 4 * h);
-          wv[q][0] = w4.x; wv[q][1] = w4.y; wv[q][2] = w4.z; wv[q][3] = w4.w;
+          const float4 w = w4[(le + q * L) * stride4 + (j >> 2) + h];
+          wv[q][0] = w.x; wv[q][1] = w.y; wv[q][2] = w.z; wv[q][3] = w.w;
         }
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           float xv[8];
-          widen8<T>(xc[r], xv);
+          widen8<T>(cur[r], xv);
 #pragma unroll
           for (int jq = 0; jq < 4; ++jq)
 #pragma unroll
@@ -287,6 +310,15 @@ __global__ __launch_bounds__(NT) void route_resident_kernel(
               acc[q][r] = __builtin_fmaf(xv[4 * h + jq], wv[q][jq], acc[q][r]);
         }
       }
+    };
+    u32x4 xa[R][XN], xb[R][XN];
+    load(xa, 0);
+    for (int jj = 0; jj < d; jj += 16) {
+      if (jj + 8 < d) load(xb, jj + 8);
+      step(xa, jj);
+      if (jj + 8 >= d) break;
+      if (jj + 16 < d) load(xa, jj + 16);
+      step(xb, jj + 8);
     }
     route_select<L, P, R>(acc, le, t0, ntok, E, k, topk_idx, topk_w);
   }
