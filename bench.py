@@ -148,6 +148,54 @@ def trace_name(kernel):
     return None
 
 
+def reference_rates(steps, warmup):
+    """Practical ceilings on this GPU, next to the published peaks: a plain
+    device copy (bytes read + written per second) and the vendor BLAS
+    (torch.matmul, hipBLASLt on ROCm) on the dense shapes of the 131072-token
+    layer. Reference measurements only; nothing in libmoe calls a library
+    GEMM."""
+    import torch
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    steps, warmup = max(steps, 5), max(warmup, 2)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    lines = []
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ms = timed(lambda: dst.copy_(src))
+    lines.append({"reference": "device copy 1 GiB", "ms": round(ms, 4),
+                  "GB/s": round(2 * n / ms / 1e6, 1)})
+    del src, dst
+    torch.manual_seed(0)
+    shapes = [("shared gate/up: x[131072,512] W[512,2048]", 131072, 512, 2048),
+              ("shared down: h[131072,1024] W[1024,512]", 131072, 1024, 512),
+              ("routed gate/up as one dense GEMM: [1048576,512] W[512,256]", 1048576, 512, 256),
+              ("routed down as one dense GEMM: [1048576,128] W[128,512]", 1048576, 128, 512),
+              ("square 8192", 8192, 8192, 8192)]
+    for label, M, K, N in shapes:
+        a = torch.randn(M, K, device=dev, dtype=torch.bfloat16)
+        bt = torch.randn(N, K, device=dev, dtype=torch.bfloat16)  # weights [N][K]
+        ms = timed(lambda: a @ bt.t())
+        tf = 2 * M * K * N / ms / 1e9
+        lines.append({"reference": f"torch.matmul bf16 {label}", "ms": round(ms, 4),
+                      "TFLOP/s": round(tf, 1), "frac_mfma_peak": round(tf / PEAK_TFLOPS["bf16"], 4)})
+        del a, bt
+    return lines
+
+
 def pmc_summary(fetch_dir, write_dir, copyf_dir, copyw_dir, workload_name, out_path):
     """HBM bytes per launch of each forward kernel from rocprofv3 FETCH_SIZE
     and WRITE_SIZE runs (KiB per dispatch), each scaled by what the same
@@ -354,6 +402,9 @@ def main():
                     help="largest train step that fits (E8 top-2 d512 h1024 bf16) and peak memory")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
+    ap.add_argument("--reference", action="store_true",
+                    help="only time reference rates on this GPU: a plain device copy and the "
+                         "vendor BLAS (torch.matmul) on this layer's GEMM shapes")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
                     help="write profiles/traffic.json from rocprofv3 --pmc output directories")
     args = ap.parse_args()
@@ -371,6 +422,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.reference:
+        for line in reference_rates(args.steps, args.warmup):
+            print(json.dumps(line), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "

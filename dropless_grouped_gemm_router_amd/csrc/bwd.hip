@@ -160,15 +160,41 @@ __global__ __launch_bounds__(kRowThreads) void router_partial_kernel(
     dv[r] = dl[s];
   }
   __syncthreads();
-  for (int j = threadIdx.x; j < d; j += kRowThreads) {
-    float acc = 0.0f;
-    for (int r = 0; r < rows; ++r) {
-      float xv;
-      if constexpr (sizeof(T) == 2) xv = bf16_to_f32(x[tok[r] * d + j]);
-      else xv = x[tok[r] * d + j];
-      acc = __builtin_fmaf(xv, dv[r], acc);
+  // Two adjacent columns per thread (d is even); eight rows' values are
+  // loaded before they are multiplied in, row order kept per column.
+  constexpr int kBatch = 8;
+  auto load2 = [&](int r, int j, float& v0, float& v1) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(x + tok[r] * d + j);
+      v0 = bf16lo(u);
+      v1 = bf16hi(u);
+    } else {
+      const float2 u = *reinterpret_cast<const float2*>(x + tok[r] * d + j);
+      v0 = u.x;
+      v1 = u.y;
     }
-    partial[static_cast<int64_t>(tile) * d + j] = acc;
+  };
+  for (int j = 2 * threadIdx.x; j < d; j += 2 * kRowThreads) {
+    float a0 = 0.0f, a1 = 0.0f;
+    int r = 0;
+    for (; r + kBatch <= rows; r += kBatch) {
+      float v0[kBatch], v1[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) load2(r + u, j, v0[u], v1[u]);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        a0 = __builtin_fmaf(v0[u], dv[r + u], a0);
+        a1 = __builtin_fmaf(v1[u], dv[r + u], a1);
+      }
+    }
+    for (; r < rows; ++r) {
+      float v0, v1;
+      load2(r, j, v0, v1);
+      a0 = __builtin_fmaf(v0, dv[r], a0);
+      a1 = __builtin_fmaf(v1, dv[r], a1);
+    }
+    partial[static_cast<int64_t>(tile) * d + j] = a0;
+    partial[static_cast<int64_t>(tile) * d + j + 1] = a1;
   }
 }
 
@@ -185,9 +211,18 @@ __global__ __launch_bounds__(kRowThreads) void router_reduce_kernel(
     cnt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
   }
   __syncthreads();
+  constexpr int kBatch = 8;
   for (int j = threadIdx.x; j < d; j += kRowThreads) {
     float acc = 0.0f;
-    for (int n = 0; n < cnt; ++n) acc += partial[static_cast<int64_t>(first + n) * d + j];
+    int n = 0;
+    for (; n + kBatch <= cnt; n += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = partial[static_cast<int64_t>(first + n + u) * d + j];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) acc += v[u];
+    }
+    for (; n < cnt; ++n) acc += partial[static_cast<int64_t>(first + n) * d + j];
     dwr[static_cast<int64_t>(j) * E + e] = acc;
   }
 }
@@ -255,20 +290,37 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
   }
 }
 
-// Fixed-order sum of split-K partials [splits][M][N]; columns n >= nsplit
-// go to c2 at column n - nsplit.
+// Fixed-order sum of split-K partials [splits][M][N] (split 0 first, fp32
+// adds); columns n >= nsplit go to c2 at column n - nsplit. Four columns per
+// thread (N and nsplit are multiples of 4) and eight partials loaded before
+// they are added, so a thread waits for memory once per eight splits.
 __global__ __launch_bounds__(kRowThreads) void split_reduce_kernel(
     const float* __restrict__ partial, int splits, int64_t M, int N, int nsplit, int64_t ldc,
     float* __restrict__ c, float* __restrict__ c2) {
-  const int64_t MN = M * N;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x; i < MN;
+  constexpr int kBatch = 8;
+  const int64_t MN = M * N, MN4 = MN / 4;
+  const float4* p4 = reinterpret_cast<const float4*>(partial);
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x; i < MN4;
        i += static_cast<int64_t>(gridDim.x) * kRowThreads) {
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) acc += partial[s * MN + i];
-    const int64_t m = i / N;
-    const int n = static_cast<int>(i % N);
-    if (n < nsplit) c[m * ldc + n] = acc;
-    else c2[m * ldc + (n - nsplit)] = acc;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    int s = 0;
+    for (; s + kBatch <= splits; s += kBatch) {
+      float4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = p4[(s + u) * MN4 + i];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
+      }
+    }
+    for (; s < splits; ++s) {
+      const float4 v = p4[s * MN4 + i];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    const int64_t m = (4 * i) / N;
+    const int n = static_cast<int>((4 * i) % N);
+    float* dst = n < nsplit ? c + m * ldc + n : c2 + m * ldc + (n - nsplit);
+    *reinterpret_cast<float4*>(dst) = acc;
   }
 }
 

@@ -109,6 +109,9 @@ int cu_count();
 // and join events; work enqueued on side() between fork(s) and join(s) runs
 // beside s, after everything enqueued on s before the fork, and s waits for
 // it from the join on.
+// Runs a call's independent part on the device's side stream. While the
+// kernel timer is on, the "side stream" is the caller's stream itself, so
+// each timed kernel runs alone and its events bracket its own duration.
 class SideFork {
  public:
   SideFork();
@@ -123,6 +126,7 @@ class SideFork {
 };
 
 // Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).
+bool trace_on();
 void trace_push(hipStream_t s, const char* name);
 void trace_pop(hipStream_t s);
 

@@ -57,6 +57,10 @@ hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices];
 SideFork::SideFork() : lock_(g_side_mu) {}
 
 hipError_t SideFork::fork(hipStream_t s) {
+  if (trace_on()) {
+    side_ = s;
+    return hipSuccess;
+  }
   hipError_t e = hipGetDevice(&dev_);
   if (e == hipSuccess && (dev_ < 0 || dev_ >= kMaxDevices)) e = hipErrorInvalidDevice;
   if (e != hipSuccess) return e;
@@ -76,6 +80,7 @@ hipError_t SideFork::fork(hipStream_t s) {
 }
 
 hipError_t SideFork::join(hipStream_t s) {
+  if (side_ == s) return hipSuccess;
   hipError_t e = hipEventRecord(g_join[dev_], side_);
   if (e == hipSuccess) e = hipStreamWaitEvent(s, g_join[dev_], 0);
   return e;

@@ -51,6 +51,8 @@ void release_marks() {
 
 }  // namespace
 
+bool trace_on() { return g_on.load(std::memory_order_relaxed); }
+
 void trace_push(hipStream_t s, const char* name) {
   if (!g_on.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(g_mu);

@@ -308,7 +308,10 @@ int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w, const moe
  * Kernel timer (host). moe_trace_enable(1) clears the record and starts
  * bracketing every libmoe kernel launch with two hipEvents on its stream;
  * moe_trace_enable(0) stops and clears. Timing adds no device work besides
- * the event records. Returns MOE_OK.
+ * the event records. While it is on, moe_forward and moe_bwd run their
+ * shared-expert part on the caller's stream instead of the side stream (the
+ * same kernels, in issue order), so every recorded duration is that of a
+ * kernel running alone. Returns MOE_OK.
  */
 int moe_trace_enable(int on);
 
