@@ -56,81 +56,118 @@ __device__ __forceinline__ void widen8<float>(const u32x4 (&v)[2], float* o) {
   }
 }
 
-// a ranks before b: valid before invalid, then larger logit, then lower index.
-__device__ __forceinline__ bool ranks_before(float av, int ae, float bv, int be) {
-  const bool a_ok = ae < 0x10000, b_ok = be < 0x10000;
-  if (a_ok != b_ok) return a_ok;
-  return (av > bv) || (av == bv && ae < be);
+// Ranking key of (logit, expert): a larger key ranks first, i.e. the larger
+// logit, then the lower expert index. The high half is the logit's bits
+// mapped to an unsigned order (-0 taken as +0, so equal logits tie), the
+// low half the complement of the index. Valid keys are never 0; 0 marks an
+// expert that does not exist or has been selected.
+__device__ __forceinline__ uint64_t rank_key(float v, int e) {
+  uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (static_cast<uint64_t>(b) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
+}
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t h = static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((h & 0x80000000u) ? (h & 0x7FFFFFFFu) : ~h);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) {
+  return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+
+// One exchange step across lanes by DPP (quad_perm [1,0,3,2] = 0xB1 and
+// [2,3,0,1] = 0x4E, row_half_mirror = 0x141, row_mirror = 0x140): plain VALU
+// moves within rows of 16 lanes, no LDS round trip.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), kCtrl, 0xF, 0xF, true));
+}
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_max_key(uint64_t k) {
+  const uint64_t o = (static_cast<uint64_t>(dpp_u32<kCtrl>(static_cast<uint32_t>(k >> 32))) << 32) |
+                     dpp_u32<kCtrl>(static_cast<uint32_t>(k));
+  return o > k ? o : k;
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __uint_as_float(dpp_u32<kCtrl>(__float_as_uint(v)));
+}
+
+// Maximum / sum over each aligned group of L lanes (L a power of two <= 16),
+// the same value in every lane of the group: after the two quad steps a
+// quad holds its result, half_mirror pairs the two quads of 8 lanes and
+// row_mirror the two halves of 16.
+template <int L>
+__device__ __forceinline__ uint64_t group_max_key(uint64_t k) {
+  static_assert(L >= 1 && L <= 16 && (L & (L - 1)) == 0, "group width");
+  if constexpr (L >= 2) k = dpp_max_key<0xB1>(k);
+  if constexpr (L >= 4) k = dpp_max_key<0x4E>(k);
+  if constexpr (L >= 8) k = dpp_max_key<0x141>(k);
+  if constexpr (L >= 16) k = dpp_max_key<0x140>(k);
+  return k;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (L >= 2) v = dpp_add<0xB1>(v);
+  if constexpr (L >= 4) v = dpp_add<0x4E>(v);
+  if constexpr (L >= 8) v = dpp_add<0x141>(v);
+  if constexpr (L >= 16) v = dpp_add<0x140>(v);
+  return v;
 }
 
 // Top-k per token from a lane's logits acc[q][r] (expert le + q L, token
-// t0 + r): k rounds of argmax, first over the lane's own P experts, then a
-// butterfly over the L lanes of the group; then the renormalised weights.
+// t0 + r): k rounds, each taking the largest remaining key of the lane's P
+// experts, then of the group's L lanes, and clearing it where it came from;
+// the lane's R tokens go through each round together. Then the renormalised
+// weights exp(l_i - l_0) / sum over the k kept ranks.
 template <int L, int P, int R>
 __device__ __forceinline__ void route_select(const float (&acc)[P][R], int le, int64_t t0,
                                              int64_t ntok, int E, int k,
                                              int32_t* __restrict__ topk_idx,
                                              float* __restrict__ topk_w) {
+  uint64_t key[R][P], mine[R][P], first[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const int e = le + q * L;
+      key[r][q] = e < E ? rank_key(acc[q][r], e) : 0;
+      mine[r][q] = 0;
+    }
+  // Rank i (< k <= L * P) is kept by lane i % L of the group, in slot i / L.
+  for (int i = 0; i < k; ++i) {
+    const int owner = i % L, slot = i / L;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      uint64_t best = key[r][0];
+#pragma unroll
+      for (int q = 1; q < P; ++q) best = key[r][q] > best ? key[r][q] : best;
+      best = group_max_key<L>(best);
+      if (i == 0) first[r] = best;
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        key[r][q] = key[r][q] == best ? 0 : key[r][q];
+        if (q == slot && le == owner) mine[r][q] = best;
+      }
+    }
+  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t t = t0 + r;
-    bool taken[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) taken[q] = (le + q * L) >= E;
-    // Rank i (< k <= L * P) is kept by lane i % L of the group, in slot i / L.
-    float my_v[P], vmax = 0.0f;
-    int my_e[P];
-#pragma unroll
-    for (int q = 0; q < P; ++q) {
-      my_v[q] = 0.0f;
-      my_e[q] = 0;
-    }
-    for (int i = 0; i < k; ++i) {
-      float bv = acc[0][r];
-      int be = taken[0] ? (0x10000 + le) : le;
-#pragma unroll
-      for (int q = 1; q < P; ++q) {
-        const int eq = le + q * L;
-        const int ce = taken[q] ? (0x10000 + eq) : eq;
-        if (ranks_before(acc[q][r], ce, bv, be)) {
-          bv = acc[q][r];
-          be = ce;
-        }
-      }
-#pragma unroll
-      for (int off = L / 2; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, L);
-        const int oe = __shfl_xor(be, off, L);
-        if (ranks_before(ov, oe, bv, be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if (i == 0) vmax = bv;
-#pragma unroll
-      for (int q = 0; q < P; ++q) {
-        if (be == le + q * L) taken[q] = true;
-        if (i == q * L + le) {
-          my_v[q] = bv;
-          my_e[q] = be;
-        }
-      }
-    }
-    // Weights exp(l_i - l_0) / sum over the k kept ranks.
+    const float vmax = key_logit(first[r]);
     float u[P], sum = 0.0f;
 #pragma unroll
     for (int q = 0; q < P; ++q) {
-      u[q] = (q * L + le < k) ? expf(my_v[q] - vmax) : 0.0f;
+      u[q] = (q * L + le < k) ? expf(key_logit(mine[r][q]) - vmax) : 0.0f;
       sum += u[q];
     }
-#pragma unroll
-    for (int off = L / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, L);
+    sum = group_sum<L>(sum);
     if (t < ntok) {
 #pragma unroll
       for (int q = 0; q < P; ++q) {
         const int i = q * L + le;
         if (i < k) {
-          topk_idx[t * k + i] = my_e[q];
+          topk_idx[t * k + i] = key_expert(mine[r][q]);
           topk_w[t * k + i] = u[q] / sum;
         }
       }

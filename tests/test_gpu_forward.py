@@ -98,6 +98,88 @@ def test_forward_deterministic(p):
     assert bool((ya == c.buf.y_sorted).all())
 
 
+def _route_only(p: Problem, seed: int, wr: np.ndarray = None):
+    """moe_route on generated tokens (and an optional replacement router);
+    returns the device routing and the oracle's (indices, weights)."""
+    import torch
+    from dropless_grouped_gemm_router_amd import binding as B
+    c = Case(p, seed=seed)
+    if wr is not None:
+        c.v["w_router"] = wr
+        c.dev["w_router"] = torch.from_numpy(wr).cuda()
+    B.moe_route(p, c.dev["x"], c.dev["w_router"], c.buf.routing)
+    torch.cuda.synchronize()
+    _, idx, w = oracle.route(c.v["x"], c.v["w_router"], p.top_k)
+    return c.routing_np(), idx, w
+
+
+# Every router lane layout: (L lanes x P experts x R tokens per lane) by
+# experts and batch size, and the chunked kernel for routers too wide for LDS
+# (64 experts at d_model 768, 32 at 1280, 8 at 5120).
+ROUTE_LAYOUTS = [
+    Problem(66000, 64, 8, 128, 64, 0, "bf16", 256),
+    Problem(40000, 64, 8, 128, 64, 0, "bf16", 256),
+    Problem(3000, 64, 8, 128, 64, 0, "bf16", 256),
+    Problem(3000, 64, 8, 128, 64, 0, "fp32", 256),
+    Problem(3000, 32, 4, 256, 64, 0, "bf16", 256),
+    Problem(3000, 16, 4, 256, 64, 0, "bf16", 256),
+    Problem(3000, 8, 2, 256, 64, 0, "bf16", 256),
+    Problem(3000, 4, 2, 256, 64, 0, "bf16", 256),
+    Problem(3000, 2, 1, 256, 64, 0, "bf16", 256),
+    Problem(3000, 64, 8, 768, 64, 0, "bf16", 256),
+    Problem(3000, 64, 8, 768, 64, 0, "fp32", 256),
+    Problem(3000, 32, 4, 1280, 64, 0, "bf16", 256),
+    Problem(1000, 8, 2, 5120, 64, 0, "bf16", 256),
+]
+
+
+@pytest.mark.parametrize("p", ROUTE_LAYOUTS, ids=pid)
+def test_route_layouts(p):
+    note(f"route layout {p}")
+    g, idx, w = _route_only(p, seed=13)
+    assert np.array_equal(g["topk_idx"], idx)
+    assert np.max(np.abs(g["topk_w"] - w)) < 2e-6
+
+
+@pytest.mark.parametrize("p", ROUTE_LAYOUTS, ids=pid)
+def test_route_exact_ties(p):
+    """Duplicated router columns give equal logits for every token: the
+    lower expert index must rank first, whether the tied experts sit in one
+    lane, in two lanes of a token's group, or far apart. The tied columns
+    are scaled up so they are usually among the top k."""
+    note(f"route ties {p}")
+    rng = np.random.default_rng(17)
+    E, d = p.experts, p.d_model
+    wr = (rng.standard_normal((d, E)) / np.sqrt(d)).astype(np.float32)
+    for e0 in range(0, E, 16):
+        for dup in (1, 4, 8, 9):
+            if e0 + dup < E:
+                wr[:, e0 + dup] = wr[:, e0]
+        wr[:, e0] *= 3.0
+        for dup in (1, 4, 8, 9):
+            if e0 + dup < E:
+                wr[:, e0 + dup] = wr[:, e0]
+    g, idx, w = _route_only(p, seed=19, wr=wr)
+    if p.top_k > 1:
+        # the ties were actually exercised
+        assert np.any((idx[:, :-1] + 1 == idx[:, 1:]) & (idx[:, :-1] % 16 == 0))
+    assert np.array_equal(g["topk_idx"], idx)
+    assert np.max(np.abs(g["topk_w"] - w)) < 2e-6
+
+
+@pytest.mark.parametrize("p", [Problem(3000, 64, 8, 128, 64, 0, "bf16", 256),
+                               Problem(66000, 64, 8, 128, 64, 0, "bf16", 256),
+                               Problem(3000, 64, 8, 768, 64, 0, "bf16", 256),
+                               Problem(500, 5, 3, 128, 64, 0, "fp32", 64)], ids=pid)
+def test_route_zero_router(p):
+    """An all-zero router: every logit is +0, so every token takes experts
+    0..k-1 in that order with weights exactly 1/k."""
+    g, idx, w = _route_only(p, seed=23, wr=np.zeros((p.d_model, p.experts), np.float32))
+    assert np.array_equal(g["topk_idx"], np.tile(np.arange(p.top_k, dtype=np.int32), (p.tokens, 1)))
+    assert np.all(g["topk_w"] == np.float32(1.0) / np.float32(p.top_k))
+    assert np.array_equal(g["topk_idx"], idx)
+
+
 def test_skewed_routing_empty_experts():
     """A router that sends every token to experts 0 and 1: two experts with
     every slot (many tiles each), the rest empty."""
