@@ -66,10 +66,57 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src0,
   }
 }
 
+// bf16 variant without LDS: one 64 x 64 tile per wave, lane 8 kb + pb
+// transposing the 8 x 8 block of source rows k0 + 8 kb + i and destination
+// rows p0 + 8 pb + j in registers. Word m of destination row j pairs rows
+// 2m and 2m + 1 of column j, i.e. the low (j even) or high (j odd) halves of
+// word j / 2 of those two source rows, one byte-select each. Eight lanes
+// read, and eight lanes write, 128 contiguous bytes of one row.
+__global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict__ src0,
+                                                        const bf16_t* __restrict__ src1,
+                                                        bf16_t* __restrict__ dst, int K, int nsrc,
+                                                        int interleave) {
+  const int ndst = interleave ? 2 * nsrc : nsrc;
+  const int tiles_p = ndst / kPackTile;
+  const int tile = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tile >= tiles_p * (K / kPackTile)) return;
+  const int lane = threadIdx.x & 63, kb = lane >> 3, pb = lane & 7;
+  const int pr = (tile % tiles_p) * kPackTile + 8 * pb;
+  const int k0 = (tile / tiles_p) * kPackTile + 8 * kb;
+  const int64_t gs = static_cast<int64_t>(K) * nsrc;
+  const bf16_t* s = src0 + blockIdx.z * gs;
+  int col = pr;
+  if (interleave) {
+    col = 16 * (pr / 32) + pr % 16;
+    if (pr % 32 >= 16) s = src1 + blockIdx.z * gs;
+  }
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = *reinterpret_cast<const u32x4*>(s + static_cast<int64_t>(k0 + i) * nsrc + col);
+  bf16_t* d = dst + blockIdx.z * static_cast<int64_t>(ndst) * K;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    u32x4 o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[m] = __builtin_amdgcn_perm(v[2 * m + 1][j / 2], v[2 * m][j / 2],
+                                   (j & 1) ? 0x07060302u : 0x05040100u);
+    *reinterpret_cast<u32x4*>(d + static_cast<int64_t>(pr + j) * K + k0) = o;
+  }
+}
+
 template <typename T>
 void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc, bool il,
           hipStream_t s) {
   const int ndst = il ? 2 * nsrc : nsrc;
+  if (std::is_same<T, bf16_t>::value) {
+    const int tiles = (ndst / kPackTile) * (K / kPackTile);
+    MOE_LAUNCH("pack_weights", pack_bf16_kernel, dim3((tiles + 3) / 4, 1, groups), dim3(256), 0, s,
+               static_cast<const bf16_t*>(s0), static_cast<const bf16_t*>(s1),
+               static_cast<bf16_t*>(dst), K, nsrc, il ? 1 : 0);
+    return;
+  }
   MOE_LAUNCH("pack_weights", pack_kernel<T>, dim3(ndst / kPackTile, K / kPackTile, groups), dim3(256), 0,
                      s, static_cast<const T*>(s0), static_cast<const T*>(s1),
                      static_cast<T*>(dst), K, nsrc, il ? 1 : 0);
