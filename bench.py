@@ -269,13 +269,19 @@ def time_steps(step, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
-def train_step_line(B, steps, warmup):
-    """Forward + backward on the train-step workload (16384 tokens)."""
+def train_step_line(B, steps, warmup, tokens=0):
+    """Forward + backward on the train-step workload (16384 tokens, or
+    `tokens` of the same layer)."""
+    import dataclasses
+
     import torch
 
     from dropless_grouped_gemm_router_amd.inputs import WORKLOADS, make_inputs
 
     name, p, _ = WORKLOADS[4]
+    if tokens:
+        p = dataclasses.replace(p, tokens=tokens)
+        name = name.replace("16384 tok", f"{tokens} tok")
     dev = B.device_inputs(make_inputs(p, seed=0, with_grad_out=True), "cuda:0")
     buf = B.allocate(p, "cuda:0", training=True, dispatch="gather")
     x, g = dev.pop("x"), dev.pop("grad_out")
@@ -286,8 +292,9 @@ def train_step_line(B, steps, warmup):
         B.backward(p, x, dev, g, buf)
 
     ms = time_steps(step, steps, warmup)
-    # per-kernel times of the same steps, from libmoe's HIP events (the
-    # shared expert's kernels overlap the routed ones in these steps)
+    # per-kernel times of the same steps, from libmoe's HIP events (with the
+    # kernel timer on, the shared expert's kernels run on the caller's
+    # stream, so each duration is that of the kernel alone)
     B.moe_trace_enable(True)
     time_steps(step, steps, 0)
     kern = B.moe_trace_summary()
@@ -400,6 +407,9 @@ def main():
                     help="time replays of one forward step captured in a HIP graph")
     ap.add_argument("--maxtok", action="store_true",
                     help="largest train step that fits (E8 top-2 d512 h1024 bf16) and peak memory")
+    ap.add_argument("--train-tokens", type=int, default=0, metavar="T",
+                    help="only time the train step (forward + backward) of the train-step layer "
+                         "at T tokens, one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB five times (counter calibration)")
     ap.add_argument("--reference", action="store_true",
@@ -442,6 +452,12 @@ def main():
     if args.maxtok:
         torch.cuda.set_device(0)
         print(json.dumps(maxtok_line(B, max(1, min(args.steps, 3)), 1)), flush=True)
+        return
+    if args.train_tokens:
+        torch.cuda.set_device(0)
+        print(json.dumps({"train_step": train_step_line(B, max(3, min(args.steps, 20)),
+                                                        max(2, args.warmup), args.train_tokens)}),
+              flush=True)
         return
 
     name, p, _ = WORKLOADS[args.workload]

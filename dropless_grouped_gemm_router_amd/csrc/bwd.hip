@@ -17,7 +17,6 @@
 // into expert order, into dY's buffer once dW_down has consumed dY.
 #include "gemm_launch.h"
 #include "gemm_wgrad.h"
-#include "sort_rows.h"
 
 namespace moe {
 
@@ -380,12 +379,13 @@ void zero(float* p, int64_t n, hipStream_t s) {
 
 
 
-// Weight gradient: bf16 operands without a row gather take the
-// transposing-LDS-read kernel, the rest the register-transposing one.
+// Weight gradient: bf16 operands take the transposing-LDS-read kernel
+// (gathering A's rows through perm when kGatherA), fp32 the
+// register-transposing one.
 template <typename T, bool kGatherA, bool kDense>
 void wgrad(const char* name, const WgradArgs& a, int groups, const void* zero, hipStream_t s) {
-  if (std::is_same<T, bf16_t>::value && !kGatherA) {
-    wgrad_tr<kDense>(name, a, groups, static_cast<const bf16_t*>(zero), s);
+  if (std::is_same<T, bf16_t>::value) {
+    wgrad_tr<kDense, kGatherA>(name, a, groups, static_cast<const bf16_t*>(zero), s);
     return;
   }
   const int64_t blocks = static_cast<int64_t>(groups) * (a.M / 128) * (a.N / 128);
@@ -508,13 +508,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
       b.lda = d;
       b.perm = r.perm;
       b.topk = k;
-      if (std::is_same<T, bf16_t>::value) {
-        // dY is dead once dW_down is out: it takes the token rows in expert order.
-        MOE_LAUNCH("bwd_sort_rows", sort_rows_kernel<T>, dim3(sort_rows_blocks(S)),
-                   dim3(kSortThreads), 0, s, static_cast<const T*>(x), r.perm, k, S, d, dY);
-        b.a = dY;
-        b.perm = nullptr;
-      }
+      b.rows_total = S;  // entries of perm
       b.b = dAB;
       b.ldb = 2 * static_cast<int64_t>(h);
       b.M = d;
@@ -526,8 +520,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
       b.nsplit = h;
       b.ldc = h;
       b.c_group_stride = static_cast<int64_t>(d) * h;
-      if (std::is_same<T, bf16_t>::value) wgrad<T, false, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
-      else wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
+      wgrad<T, true, false>("bwd_wgrad_gate_up", b, E, zero_row, s);
     }
   };
   auto shared_bwd = [&](hipStream_t s) {

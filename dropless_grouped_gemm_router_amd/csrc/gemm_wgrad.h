@@ -17,6 +17,14 @@
 // holds no other memory operation, so waiting for vmcnt <= loads of NS - 2
 // stages leaves the next NS - 2 stages in flight while one is multiplied.
 //
+// Gathered A (kGather): row r of A is token perm[r] / topk of x. Each wave
+// fetches the 64 perm entries of a stage into its own LDS slot by one more
+// direct-to-LDS load per stage (so the per-stage load count stays the same
+// for every wave and the counted waits stay exact), NS - 1 stages before
+// that stage's row loads are issued, and reads them back by inline-assembly
+// LDS reads when it forms the row addresses. Tokens are clamped to the
+// table, so no address leaves x whatever an entry holds.
+//
 // Group g covers rows [row_offsets[g], row_offsets[g+1]) (clipped to cap
 // rows under capacity routing), or the g-th of `splits` equal slices of
 // rows_total (dense split-K partials, reduced later in a fixed order). One
@@ -48,7 +56,7 @@ struct TrCfg {
   static constexpr int B_LOADS = B_BYTES / 1024 / (NT / 64);
   static constexpr int LOADS = A_LOADS + B_LOADS;
   static_assert(A_BYTES % (1024 * (NT / 64)) == 0 && B_BYTES % (1024 * (NT / 64)) == 0, "loads");
-  static_assert(NS >= 2 && NS * STAGE <= 160 * 1024, "LDS");
+  static_assert(NS >= 2 && NS * STAGE + NS * (NT / 64) * 256 <= 160 * 1024, "LDS");
 };
 
 // Chunk position of logical 16-byte chunk c of LDS row r.
@@ -78,6 +86,53 @@ __device__ __forceinline__ void tr_issue(char* lds_op, const bf16_t* base, int64
     const int64_t row = row0 + r;
     const bf16_t* src = row < row_end ? base + row * ld + col0 + c * 8 : zero + c * 8;
     __builtin_amdgcn_global_load_lds(src, lds_op + blk * 1024, 16, 0, 0);
+  }
+}
+
+// One stage's 64 perm entries (rows row_start ..) into a 256-byte LDS slot,
+// lane l's entry at byte 4 l; entries past the table repeat its last one.
+__device__ __forceinline__ void tr_issue_idx(char* slot, const int32_t* perm, int64_t row_start,
+                                             int64_t len, int lane) {
+  int64_t r = row_start + lane;
+  r = r < len ? r : len - 1;
+  __builtin_amdgcn_global_load_lds(perm + r, slot, 4, 0, 0);
+}
+
+// A-operand loads of one stage with gathered rows: as tr_issue, the row's
+// address taken from token perm[row] / topk (read from the stage's slot at
+// LDS byte address idx_lds), clamped to [0, ntok).
+template <int CPR, int LOADS_OP>
+__device__ __forceinline__ void tr_issue_gather(char* lds_op, const bf16_t* x, int64_t ld,
+                                                int col0, int64_t row0, int64_t row_end,
+                                                const bf16_t* zero, uint32_t idx_lds, int topk,
+                                                int64_t ntok, int wave, int lane) {
+  static_assert(LOADS_OP == 4, "four A loads per wave per stage");
+  int rr[4], pos[4];
+  uint32_t ad[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int ci = (wave * LOADS_OP + u) * 64 + lane;
+    rr[u] = ci / CPR;
+    pos[u] = ci % CPR;
+    ad[u] = idx_lds + 4 * rr[u];
+  }
+  int v[4];
+  asm volatile(
+      "ds_read_b32 %0, %4\n\t"
+      "ds_read_b32 %1, %5\n\t"
+      "ds_read_b32 %2, %6\n\t"
+      "ds_read_b32 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int64_t tok = v[u] / topk;
+    tok = tok < 0 ? 0 : (tok >= ntok ? ntok - 1 : tok);
+    const int c = tr_swz(rr[u], pos[u]);
+    const bf16_t* src = row0 + rr[u] < row_end ? x + tok * ld + col0 + c * 8 : zero + c * 8;
+    __builtin_amdgcn_global_load_lds(src, lds_op + (wave * LOADS_OP + u) * 1024, 16, 0, 0);
   }
 }
 
@@ -116,11 +171,13 @@ __device__ __forceinline__ void tr_read_kstep(const uint32_t (&ad)[8], tr_v4i16 
       : "memory");
 }
 
-template <typename Cfg, bool kDense>
+template <typename Cfg, bool kDense, bool kGather>
 __global__ __launch_bounds__(Cfg::NT) void wgrad_tr_kernel(const WgradArgs p,
                                                            const bf16_t* __restrict__ zero) {
   constexpr int BM = Cfg::BM, BN = Cfg::BN, NS = Cfg::NS;
-  __shared__ __attribute__((aligned(1024))) char smem[NS * Cfg::STAGE];
+  constexpr int kIdxSlots = kGather ? NS * (Cfg::NT / 64) : 0;  // NS slots of 256 B per wave
+  constexpr int kLoads = Cfg::LOADS + (kGather ? 1 : 0);         // per wave per stage
+  __shared__ __attribute__((aligned(1024))) char smem[NS * Cfg::STAGE + kIdxSlots * 256];
 
   const int tiles_m = p.M / BM, tiles_n = p.N / BN;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -165,21 +222,43 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad_tr_kernel(const WgradArgs p,
   // LDS byte address of smem (the low 32 bits of its generic address).
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
   const int nk = static_cast<int>((r1 - r0 + kTrKT - 1) / kTrKT);
+  // Gather: this wave's perm slots (slot t % NS holds stage t's entries,
+  // fetched with the loads of stage t - NS + 1).
+  char* idx_slots = smem + NS * Cfg::STAGE + wave * NS * 256;
+  const uint32_t idx_lds = lds_base + NS * Cfg::STAGE + wave * NS * 256;
+  const int64_t ntok = kGather ? p.rows_total / p.topk : 0;
   auto issue = [&](int st) {
     char* buf = smem + (st % NS) * Cfg::STAGE;
     const int64_t row0 = r0 + static_cast<int64_t>(st) * kTrKT;
-    tr_issue<Cfg::A_CPR, Cfg::A_LOADS>(buf, A, p.lda, a_col, row0, r1, zero, wave, lane);
+    if (kGather) {
+      tr_issue_idx(idx_slots + ((st + NS - 1) % NS) * 256, p.perm,
+                   r0 + static_cast<int64_t>(st + NS - 1) * kTrKT, p.rows_total, lane);
+      tr_issue_gather<Cfg::A_CPR, Cfg::A_LOADS>(buf, A, p.lda, a_col, row0, r1, zero,
+                                                idx_lds + (st % NS) * 256, p.topk, ntok, wave,
+                                                lane);
+    } else {
+      tr_issue<Cfg::A_CPR, Cfg::A_LOADS>(buf, A, p.lda, a_col, row0, r1, zero, wave, lane);
+    }
     tr_issue<Cfg::B_CPR, Cfg::B_LOADS>(buf + Cfg::A_BYTES, B, p.ldb, b_col, row0, r1, zero, wave,
                                        lane);
   };
+  if (kGather) {
+    // the entries of stages 0 .. NS - 2, landed before their row loads
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      tr_issue_idx(idx_slots + st * 256, p.perm, r0 + static_cast<int64_t>(st) * kTrKT,
+                   p.rows_total, lane);
+    tr_wait_vm<0>();
+  }
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st) issue(st);
 
   for (int s = 0; s < nk; ++s) {
     // This wave's part of stage s has landed once at most NS - 2 stages'
     // loads remain; the barrier makes every wave's part visible and frees
-    // the buffer multiplied in iteration s - 1 for stage s + NS - 1.
-    tr_wait_vm<Cfg::LOADS * (NS - 2)>();
+    // the buffer multiplied in iteration s - 1 for stage s + NS - 1. (With
+    // a gather, stage s + NS - 1's perm entries came with stage s's loads.)
+    tr_wait_vm<kLoads * (NS - 2)>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     issue(s + NS - 1);
     const uint32_t buf = lds_base + (s % NS) * Cfg::STAGE;
@@ -235,20 +314,23 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad_tr_kernel(const WgradArgs p,
 
 // Launch over (group, M tile, N tile); M a multiple of 128 (256 taken when it
 // divides), N a multiple of 128; `zero` a kTrZeroBytes zero buffer.
-template <bool kDense>
+// kGather: a.perm (a.rows_total entries, at least one) maps rows to slots,
+// token = slot / a.topk.
+template <bool kDense, bool kGather = false>
 void wgrad_tr(const char* name, const WgradArgs& a, int groups, const bf16_t* zero,
               hipStream_t s) {
+  if (kGather && a.rows_total < 1) return;
   if (a.M % 256 == 0) {
     using Cfg = TrCfg<256, 3>;
     const int64_t blocks = static_cast<int64_t>(groups) * (a.M / 256) * (a.N / 128);
     if (blocks <= 0) return;
-    MOE_LAUNCH(name, (wgrad_tr_kernel<Cfg, kDense>), dim3(static_cast<unsigned>(blocks)),
+    MOE_LAUNCH(name, (wgrad_tr_kernel<Cfg, kDense, kGather>), dim3(static_cast<unsigned>(blocks)),
                dim3(Cfg::NT), 0, s, a, zero);
   } else {
     using Cfg = TrCfg<128, 4>;
     const int64_t blocks = static_cast<int64_t>(groups) * (a.M / 128) * (a.N / 128);
     if (blocks <= 0) return;
-    MOE_LAUNCH(name, (wgrad_tr_kernel<Cfg, kDense>), dim3(static_cast<unsigned>(blocks)),
+    MOE_LAUNCH(name, (wgrad_tr_kernel<Cfg, kDense, kGather>), dim3(static_cast<unsigned>(blocks)),
                dim3(Cfg::NT), 0, s, a, zero);
   }
 }
