@@ -134,7 +134,7 @@ def trace_name(kernel):
     for k in ("count", "scan", "scatter"):
         if f"{k}_kernel" in kernel:
             return f"permute_{k}"
-    if "pack_kernel" in kernel:
+    if "pack_kernel" in kernel or "pack_bf16_kernel" in kernel:
         return "pack_weights"
     if "sort_rows_kernel" in kernel:
         return "sort_rows"
