@@ -158,8 +158,24 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   a.sa = sa;
   a.sb = sb;
   a.lds = 2 * static_cast<int64_t>(p.d_hidden);
-  if (x_sorted) grouped_gemm<T, false, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
-  else grouped_gemm<T, true, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
+  // 256-row tile list (by expert, from the offsets) when block_m is smaller
+  // and the experts are full enough: the down GEMM always, the gate/up GEMM
+  // when it also saves the pre-activations (three outputs, which the wide
+  // engine parks and stores as whole row pieces).
+  int32_t* t256 = static_cast<int32_t*>(tiles256);
+  const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
+  const bool retiled = retile_rows(p);
+  if (retiled) launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
+  if (retiled && sa && !x_sorted && wide_fits<T>(a)) {
+    GemmArgs a256 = a;
+    a256.tiles = t256 + 4;
+    a256.num_tiles = t256;
+    grouped_gemm<T, true, kEpiSwiglu>("gemm_gate_up", a256, kRetileBm, mt256, s);
+  } else if (x_sorted) {
+    grouped_gemm<T, false, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
+  } else {
+    grouped_gemm<T, true, kEpiSwiglu>("gemm_gate_up", a, p.block_m, max_tiles, s);
+  }
 
   GemmArgs b{};
   b.a = h_sorted;
@@ -172,12 +188,9 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   b.num_tiles = r.num_tiles;
   b.c = y_sorted;
   b.ldc = p.d_model;
-  if (retile_rows(p) && wide_fits<T>(b)) {
+  if (retiled && wide_fits<T>(b)) {
     // 256-row tiles on the wide engine for the down GEMM (its output stores
     // dominate, and the wide engine parks them as whole row pieces)
-    int32_t* t256 = static_cast<int32_t*>(tiles256);
-    const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
-    launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
     b.tiles = t256 + 4;
     b.num_tiles = t256;
     grouped_gemm<T, false, kEpiStore>("gemm_down", b, kRetileBm, mt256, s);

@@ -434,9 +434,11 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
       buf ^= 1;
     }
 
-    if (kEpi != kEpiStore && kEpi != kEpiCombine) {
-      // SwiGLU outputs are half the tile (or read saved values): stored
-      // straight from the accumulators.
+    if (kEpi != kEpiStore && kEpi != kEpiCombine && !(kEpi == kEpiSwiglu && p.sa)) {
+      // The SwiGLU output alone is half the tile (and the SwiGLU backward
+      // reads saved values): stored straight from the accumulators. With the
+      // pre-activations saved as well (three outputs) the parked path below
+      // is faster.
       gemm_epilogue<bf16_t, WideCfg, kEpi>(p, acc, cur.row0, cur.rows, nt, wm, wn, g, r32);
     } else {
       // The buffer of the last stage is free once every wave is done with it
