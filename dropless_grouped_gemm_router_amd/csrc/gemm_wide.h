@@ -227,6 +227,39 @@ __device__ __forceinline__ void wide_drain_combine(const GemmArgs& p, const char
   }
 }
 
+// SwiGLU backward through LDS: region row r holds 32 fp32 values of dH
+// (16-byte chunk c at c ^ (r & 7)); lane l takes rows l / 8 + 8 k and the
+// four columns 4 (l % 8) of the pass, so eight lanes load the saved gate and
+// up values and store dA and dB as 64 contiguous bytes of a row. The same
+// formulas as the accumulator-layout epilogue.
+__device__ __forceinline__ void wide_drain_swiglu_bwd(const GemmArgs& p, const char* region,
+                                                      int64_t orow, int col, int rows, int lane) {
+  const bf16_t* sa = static_cast<const bf16_t*>(p.sa);
+  const bf16_t* sb = static_cast<const bf16_t*>(p.sb);
+  bf16_t* c = static_cast<bf16_t*>(p.c);
+  const int ch = lane & 7;
+  const int n = col + 4 * ch;
+#pragma unroll 2
+  for (int k = 0; k < 8; ++k) {
+    const int r = k * 8 + (lane >> 3);
+    if (r >= rows) break;
+    const float4 dh = *reinterpret_cast<const float4*>(region + r * 128 + ((ch ^ (r & 7)) << 4));
+    float a[4], b[4];
+    load4(sa + (orow + r) * p.lds + n, a);
+    load4(sb + (orow + r) * p.lds + n, b);
+    const float dv[4] = {dh.x, dh.y, dh.z, dh.w};
+    float da[4], db[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float sg = sigmoid_f(a[q]);
+      da[q] = dv[q] * b[q] * sg * (1.0f + a[q] * (1.0f - sg));
+      db[q] = dv[q] * a[q] * sg;
+    }
+    store4(c + (orow + r) * p.ldc + n, da[0], da[1], da[2], da[3]);
+    store4(c + (orow + r) * p.ldc + p.hsplit + n, db[0], db[1], db[2], db[3]);
+  }
+}
+
 // Parks the wave's 64 x 64 block of SwiGLU results (kWhich 0), gate
 // pre-activations (1) or up pre-activations (2). Packed columns j*32 +
 // [0,16) are gate columns and j*32 + [16,32) the matching up columns, so
@@ -288,6 +321,21 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
                       a[4 * rr + 2], a[4 * rr + 3]);
           }
       wide_drain_combine(p, region, comb, orow, nt * WideCfg::BN + wn * 128 + h * 64, wrows, lane);
+    }
+  } else if (kEpi == kEpiSwigluBwd) {
+    // Four passes of 32 columns (MFMA tile j = h), dH parked as fp32.
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = i * 32 + r32, chunk = 2 * rr + g;
+          *reinterpret_cast<float4*>(region + row * 128 + ((chunk ^ (row & 7)) << 4)) =
+              make_float4(acc[i][h][4 * rr], acc[i][h][4 * rr + 1], acc[i][h][4 * rr + 2],
+                          acc[i][h][4 * rr + 3]);
+        }
+      wide_drain_swiglu_bwd(p, region, orow, nt * WideCfg::BN + wn * 128 + h * 32, wrows, lane);
     }
   } else if (kEpi == kEpiStore) {
     // Two passes of 64 columns (MFMA tiles j = 2h, 2h + 1).
@@ -434,11 +482,11 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
       buf ^= 1;
     }
 
-    if (kEpi != kEpiStore && kEpi != kEpiCombine && !(kEpi == kEpiSwiglu && p.sa)) {
-      // The SwiGLU output alone is half the tile (and the SwiGLU backward
-      // reads saved values): stored straight from the accumulators. With the
-      // pre-activations saved as well (three outputs) the parked path below
-      // is faster.
+    if (kEpi == kEpiSwiglu && !p.sa) {
+      // The SwiGLU output alone is half the tile: stored straight from the
+      // accumulators. With the pre-activations saved as well (three
+      // outputs), and for the SwiGLU backward, the parked path below is
+      // faster.
       gemm_epilogue<bf16_t, WideCfg, kEpi>(p, acc, cur.row0, cur.rows, nt, wm, wn, g, r32);
     } else {
       // The buffer of the last stage is free once every wave is done with it
