@@ -105,3 +105,34 @@ def test_train_step_replays_from_a_hip_graph():
         replayed = snapshot()
         for a, b in zip(eager, replayed):
             assert bits_equal(a, b)
+
+
+def test_kernel_timer_mode_gives_the_same_bits():
+    """With libmoe's kernel timer on, moe_forward and moe_bwd run the shared
+    expert's part on the caller's stream (so every recorded duration is a
+    kernel's own): the same kernels in issue order, so the same bits as the
+    two-stream call, and every kernel of the step is recorded."""
+    import torch
+    p = Problem(1500, 8, 2, 256, 128, 128, "bf16", 128)
+    c = Case(p, seed=37, training=True)
+    w = c.weights()
+    buf = B.allocate(p, training=True, dispatch="gather")
+
+    def step():
+        B.forward_dispatch(p, "gather", c.dev["x"], w, buf, training=True)
+        B.backward(p, c.dev["x"], w, c.dev["grad_out"], buf)
+        torch.cuda.synchronize()
+        return [buf.out.clone(), buf.grad_x.clone()] + [t.clone() for t in buf.grads.values()]
+
+    plain = step()
+    B.moe_trace_enable(True)
+    try:
+        timed = step()
+        kern = B.moe_trace_summary()
+    finally:
+        B.moe_trace_enable(False)
+    for a, b in zip(plain, timed):
+        assert bits_equal(a, b)
+    for name in ("route", "gemm_gate_up", "gemm_down", "shared_gate_up", "shared_down", "combine",
+                 "bwd_combine", "bwd_shared_down_dgrad", "bwd_wgrad_gate_up", "bwd_dx"):
+        assert name in kern and kern[name]["count"] >= 1, name
