@@ -55,6 +55,9 @@ SMALL = [
     # a 256-row tile list derived from the offsets (capacity-clipped too)
     Problem(20000, 8, 2, 256, 128, 128, "bf16", 128),
     Problem(20000, 8, 2, 256, 128, 0, "bf16", 64, capacity=4000),
+    # the largest d_model the library takes, and every expert selected
+    Problem(64, 8, 2, 8192, 128, 0, "bf16", 64),
+    Problem(300, 64, 64, 128, 128, 128, "bf16", 64),
     # capacity routing: dropped slots give no expert gradient but still a
     # router gradient
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),

@@ -51,6 +51,12 @@ SMALL = [
     # a 256-row tile list derived from the offsets (capacity-clipped too)
     Problem(20000, 8, 2, 256, 128, 0, "bf16", 64),
     Problem(20000, 8, 2, 256, 128, 128, "bf16", 128, capacity=4000),
+    # the largest d_model the library takes (K = 8192 in the gate/up GEMM,
+    # the router streamed through LDS in chunks) and every expert selected
+    # (top_k = E = 64: the combine past eight ranks)
+    Problem(64, 8, 2, 8192, 64, 0, "bf16", 64),
+    Problem(64, 8, 2, 8192, 64, 0, "fp32", 64),
+    Problem(300, 64, 64, 128, 64, 64, "bf16", 64),
     # capacity routing: the busier experts drop their last slots
     Problem(1500, 8, 2, 256, 128, 128, "bf16", 256, capacity=300),
     Problem(517, 16, 4, 256, 192, 128, "fp32", 32, capacity=100),
