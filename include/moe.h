@@ -30,7 +30,8 @@
  *   - All argument checks run on the host before anything is enqueued; a
  *     call that returns an error has enqueued nothing (MOE_ERR_HIP aside,
  *     which reports a failed launch).
- *   - tokens == 0 is a successful no-op.
+ *   - tokens == 0 is a successful no-op, except that moe_bwd then zeroes
+ *     the weight gradients (the gradient of an empty batch).
  *   - Values inside device buffers are not checked: an out-of-range expert
  *     index passed to moe_permute, or a routing state not produced by
  *     moe_route/moe_permute for the same problem, is undefined behaviour.
