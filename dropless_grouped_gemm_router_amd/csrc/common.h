@@ -24,16 +24,22 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest even; NaN inputs stay NaN (quiet bit forced).
+// Round to nearest even; NaN inputs stay NaN (quiet bit forced). gfx950
+// converts in hardware (v_cvt_pk_bf16_f32, two values per instruction):
+// over all 2^32 fp32 inputs it gives the same bits as the integer rounding
+// (add 0x7fff plus the lowest kept bit, keep the high half; NaN: high half
+// with the quiet bit set), which costs about six VALU instructions and two
+// exec-mask branches per value.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_hw v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
 }
 
 // Low / high bf16 of a packed pair, widened exactly.
