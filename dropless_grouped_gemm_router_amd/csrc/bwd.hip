@@ -437,7 +437,7 @@ void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing&
     // 256-row tiles on the wide engine (K = 2h, N = d_model)
     int32_t* t256 = static_cast<int32_t*>(tiles256);
     const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
-    launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
+    (void)launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
     b.tiles = t256 + 4;
     b.num_tiles = t256;
     grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, kRetileBm, mt256, s);

@@ -157,6 +157,7 @@ hipError_t launch_permute(int64_t T, int k, int E, int bm, int cap, const int32_
 
 // 256-row tile list for the GEMMs that run faster on the wide engine than
 // on the caller's block_m (see retile_rows), from the expert offsets.
+// Returns hipPeekAtLastError(): a launch error is left pending, not cleared.
 hipError_t launch_retile(const int32_t* offsets, int E, int bm2, int cap, int32_t* tiles,
                          int32_t* num_tiles, hipStream_t s);
 constexpr int kRetileBm = 256;

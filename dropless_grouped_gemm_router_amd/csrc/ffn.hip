@@ -165,7 +165,7 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   int32_t* t256 = static_cast<int32_t*>(tiles256);
   const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
   const bool retiled = retile_rows(p);
-  if (retiled) launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
+  if (retiled) (void)launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
   if (retiled && sa && !x_sorted && wide_fits<T>(a)) {
     GemmArgs a256 = a;
     a256.tiles = t256 + 4;

@@ -285,7 +285,9 @@ hipError_t launch_retile(const int32_t* offsets, int E, int bm2, int cap, int32_
                          int32_t* num_tiles, hipStream_t s) {
   MOE_LAUNCH("retile", retile_kernel, dim3(1), dim3(kScanThreads), 0, s, offsets, E, bm2, cap,
              tiles, num_tiles);
-  return hipGetLastError();
+  // Called in the middle of a stage: the error stays pending for the
+  // stage's own final hipGetLastError().
+  return hipPeekAtLastError();
 }
 
 size_t permute_ws_bytes(int64_t S, int E) {
