@@ -159,14 +159,13 @@ void routed_ffn(const moe_problem& p, const void* x, const moe_routing& r, const
   a.sb = sb;
   a.lds = 2 * static_cast<int64_t>(p.d_hidden);
   // 256-row tile list (by expert, from the offsets) when block_m is smaller
-  // and the experts are full enough: the down GEMM always, the gate/up GEMM
-  // when it also saves the pre-activations (three outputs, which the wide
-  // engine parks and stores as whole row pieces).
+  // and the experts are full enough: both GEMMs then run on the wide engine
+  // (the gate/up GEMM whenever it gathers its rows).
   int32_t* t256 = static_cast<int32_t*>(tiles256);
   const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
   const bool retiled = retile_rows(p);
   if (retiled) (void)launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
-  if (retiled && sa && !x_sorted && wide_fits<T>(a)) {
+  if (retiled && !x_sorted && wide_fits<T>(a)) {
     GemmArgs a256 = a;
     a256.tiles = t256 + 4;
     a256.num_tiles = t256;

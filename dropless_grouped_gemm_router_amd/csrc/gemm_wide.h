@@ -482,21 +482,15 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
       buf ^= 1;
     }
 
-    if (kEpi == kEpiSwiglu && !p.sa) {
-      // The SwiGLU output alone is half the tile: stored straight from the
-      // accumulators. With the pre-activations saved as well (three
-      // outputs), and for the SwiGLU backward, the parked path below is
-      // faster.
-      gemm_epilogue<bf16_t, WideCfg, kEpi>(p, acc, cur.row0, cur.rows, nt, wm, wn, g, r32);
-    } else {
-      // The buffer of the last stage is free once every wave is done with it
-      // (the other one is receiving the next item's first stage).
-      wide_barrier();
-      wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192,
-                          kEpi == kEpiCombine ? smem + 2 * kWideStage + wave * 4096 : nullptr,
-                          cur.row0, cur.rows, nt, wm, wn, g,
-                          r32, lane);
-    }
+    // Every epilogue goes through LDS, whole 128-byte row pieces per store
+    // (for the SwiGLU output alone too: 8-byte stores straight from the
+    // accumulators touch 32 rows per instruction and were 3-4 % slower).
+    // The buffer of the last stage is free once every wave is done with it
+    // (the other one is receiving the next item's first stage).
+    wide_barrier();
+    wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192,
+                        kEpi == kEpiCombine ? smem + 2 * kWideStage + wave * 4096 : nullptr,
+                        cur.row0, cur.rows, nt, wm, wn, g, r32, lane);
 
     if (nxt.rows <= 0) break;
     w = w1;
