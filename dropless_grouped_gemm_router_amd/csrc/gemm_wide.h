@@ -158,11 +158,16 @@ __device__ __forceinline__ void wide_park(char* region, int row, int byte, float
 }
 
 // Writes the parked block: region row r goes to dst + r * ld (elements),
-// 64 bf16 columns, for rows r < rows.
+// 64 bf16 columns, for rows r < rows; rows may be 0 or negative (a wave
+// block past the tile's end), with dst + (rows - 1) * ld then the tile's
+// last row. Every lane issues exactly eight stores: a row r >= rows was
+// computed from a repeat of the tile's last row (wide_src_rows), so its
+// values are that row's, bit for bit, and it is written over that row.
+// The fixed store count lets the next item's first wait leave these
+// stores in flight (wide_wait_stores).
 __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int64_t ld, int rows,
                                            int lane) {
-  // All eight LDS reads first (always in bounds), then the row-guarded
-  // stores: a guarded read-store pair per row would wait out each read.
+  // All eight LDS reads first (always in bounds), then the stores.
   const int c = lane & 7;
   u32x4 v[8];
 #pragma unroll
@@ -173,8 +178,27 @@ __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int6
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int r = k * 8 + (lane >> 3);
-    if (r < rows) *reinterpret_cast<u32x4*>(dst + r * ld + c * 8) = v[k];
+    *reinterpret_cast<u32x4*>(dst + min(r, rows - 1) * ld + c * 8) = v[k];
   }
+}
+
+// Global stores a wave's epilogue issues per item through wide_drain (8
+// per call), or 0 where the epilogue's store count varies (the gather-sum
+// and SwiGLU-backward drains skip rows past the tile's end).
+template <int kEpi>
+__device__ __forceinline__ int wide_epilogue_stores(const GemmArgs& p) {
+  return kEpi == kEpiStore ? 16 : (kEpi == kEpiSwiglu ? (p.sa ? 24 : 8) : 0);
+}
+
+// First wait of an item whose predecessor's epilogue issued n stores after
+// this item's first stage loads. vmcnt counts a wave's loads and stores in
+// issue order, so vmcnt(n) sees those loads land and leaves the stores in
+// flight during the first stage; lgkmcnt(0) as in wide_wait_all.
+__device__ __forceinline__ void wide_wait_stores(int n) {
+  if (n == 8) __builtin_amdgcn_s_waitcnt(8 | (0x7 << 4));
+  else if (n == 16) __builtin_amdgcn_s_waitcnt(0 | (1 << 14) | (0x7 << 4));
+  else if (n == 24) __builtin_amdgcn_s_waitcnt(8 | (1 << 14) | (0x7 << 4));
+  else wide_wait_all();
 }
 
 // Fused gather-sum drain (kEpiCombine, dense rows = tokens): region row r
@@ -442,6 +466,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
 
   int buf = 0;
   wide_issue(smem, a_cur, b1_cur, b_off, b_step, 0, wave);
+  int stores_out = 0;  // stores the previous item's epilogue left in flight
 
   while (true) {
     const int nt = w % n_tiles_n;
@@ -457,7 +482,8 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
     for (int s = 0; s < nk; ++s) {
-      wide_wait_all();
+      if (s == 0) wide_wait_stores(stores_out);
+      else wide_wait_all();
       wide_barrier();
       char* nb = smem + (buf ^ 1) * kWideStage;
       // The next item's metadata and row indices are read during this
@@ -491,6 +517,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
     wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192,
                         kEpi == kEpiCombine ? smem + 2 * kWideStage + wave * 4096 : nullptr,
                         cur.row0, cur.rows, nt, wm, wn, g, r32, lane);
+    stores_out = wide_epilogue_stores<kEpi>(p);
 
     if (nxt.rows <= 0) break;
     w = w1;
