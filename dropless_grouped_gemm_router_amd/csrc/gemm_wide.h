@@ -148,13 +148,21 @@ __device__ __forceinline__ void wide_b_bases(const GemmArgs& p, const TileInfo& 
 // region and stores it back as whole 128-byte row pieces (64 lanes x 16
 // bytes = 8 rows per instruction). Chunk c of region row r sits at position
 // c ^ (r & 7), so the accumulator-layout writes spread over the banks.
+// The park writes and the drain's reads are inline assembly: the compiler
+// takes any plain LDS access as possibly aliasing the next item's first
+// stage, which is in flight by direct-to-LDS loads, and would wait for all
+// of it first. (The region is the other stage buffer; the next item's first
+// wait covers those loads.)
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
 __device__ __forceinline__ void wide_park(char* region, int row, int byte, float v0, float v1,
                                           float v2, float v3) {
   const int pos = (((byte >> 4) ^ (row & 7)) << 4) | (byte & 15);
-  uint2 u;
-  u.x = pack_bf16x2(v0, v1);
-  u.y = pack_bf16x2(v2, v3);
-  *reinterpret_cast<uint2*>(region + row * 128 + pos) = u;
+  const uint64_t d = static_cast<uint64_t>(pack_bf16x2(v0, v1)) |
+                     (static_cast<uint64_t>(pack_bf16x2(v2, v3)) << 32);
+  asm volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(region + row * 128 + pos)), "v"(d) : "memory");
 }
 
 // Writes the parked block: region row r goes to dst + r * ld (elements),
@@ -169,12 +177,28 @@ __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int6
                                            int lane) {
   // All eight LDS reads first (always in bounds), then the stores.
   const int c = lane & 7;
-  u32x4 v[8];
+  uint32_t ad[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int r = k * 8 + (lane >> 3);
-    v[k] = *reinterpret_cast<const u32x4*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+    ad[k] = lds_addr(region + r * 128 + ((c ^ (r & 7)) << 4));
   }
+  u32x4 v[8];
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b128 %4, %12\n\t"
+      "ds_read_b128 %5, %13\n\t"
+      "ds_read_b128 %6, %14\n\t"
+      "ds_read_b128 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7])
+      : "memory");
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int r = k * 8 + (lane >> 3);
