@@ -345,6 +345,11 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
   const int64_t orow = static_cast<int64_t>(row0) + wm * 64;
   bf16_t* c = static_cast<bf16_t*>(p.c);
   if (kEpi == kEpiCombine) {
+    // Its drain reads the parked rows with plain LDS loads between its row
+    // gathers; after this wait the compiler knows the next item's stage
+    // loads have landed and keeps the gathers pipelined instead of waiting
+    // for all of them before every LDS read.
+    wide_wait_all();
     // The block's 64 tokens own 64 k consecutive entries of ginv and gw.
     const int K = p.gk;
     const int valid = (wrows < 64 ? (wrows > 0 ? wrows : 0) : 64) * K;
