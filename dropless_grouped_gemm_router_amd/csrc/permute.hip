@@ -115,13 +115,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
   }
   __syncthreads();
   int32_t run = wsum[wave] + incl - local;
+  // Entry e * nblk is block 0 of expert e: the first such entry at or after
+  // b0, found with one division; later ones follow every nblk entries.
+  int e_next = static_cast<int>((b0 + nblk - 1) / nblk);
+  int64_t i_next = static_cast<int64_t>(e_next) * nblk;
   if (whole) {
     int32_t ex[kScanRegs];
 #pragma unroll
     for (int q = 0; q < kScanRegs; ++q) {
       const int64_t i = b0 + q;
       ex[q] = run;
-      if (i % nblk == 0) off[i / nblk] = run;  // block 0 of expert i / nblk
+      if (i == i_next) {
+        off[e_next] = run;
+        ++e_next;
+        i_next += nblk;
+      }
       run += vals[q];
     }
 #pragma unroll
@@ -134,7 +142,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
       const int64_t i = b0 + q;
       if (i < b1) {
         blk_counts[i] = run;
-        if (i % nblk == 0) off[i / nblk] = run;  // block 0 of expert i / nblk
+        if (i == i_next) {
+          off[e_next] = run;
+          ++e_next;
+          i_next += nblk;
+        }
         run += vals[q];
       }
     }
@@ -142,7 +154,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
     for (int64_t i = b0; i < b1; ++i) {
       const int32_t v = blk_counts[i];
       blk_counts[i] = run;
-      if (i % nblk == 0) off[i / nblk] = run;
+      if (i == i_next) {
+        off[e_next] = run;
+        ++e_next;
+        i_next += nblk;
+      }
       run += v;
     }
   }
