@@ -55,6 +55,27 @@ __device__ __forceinline__ int32_t kept_rows(int32_t count, int cap) {
 
 // One workgroup: in-place exclusive scan of blk_counts[E * nblk], then the
 // expert offsets and the tile list.
+// Tile offsets of the experts (E <= 64, so one wave): lane e counts its
+// expert's tiles of bm rows over its kept rows (rows_e), an inclusive scan
+// over the lanes gives every expert's first tile, and lane 63 holds the
+// total. Called by the first wave only.
+__device__ __forceinline__ void wave_tile_offsets(int32_t rows_e, int E, int bm,
+                                                  int32_t* tile_off, int32_t* num_tiles) {
+  const int e = threadIdx.x;
+  const int32_t cnt = e < E ? (rows_e + bm - 1) / bm : 0;
+  int32_t incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t v = __shfl_up(incl, o, 64);
+    if (e >= o) incl += v;
+  }
+  if (e < E) tile_off[e] = incl - cnt;
+  if (e == 63) {
+    tile_off[E] = incl;
+    *num_tiles = incl;
+  }
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict__ blk_counts,
                                                             int nblk, int E, int bm, int cap,
                                                             int64_t S,
@@ -163,15 +184,11 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(int32_t* __restrict_
     }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    off[E] = static_cast<int32_t>(S);
-    int32_t nt = 0;
-    for (int e = 0; e < E; ++e) {
-      tile_off[e] = nt;
-      nt += (kept_rows(off[e + 1] - off[e], cap) + bm - 1) / bm;
-    }
-    tile_off[E] = nt;
-    *num_tiles = nt;
+  if (threadIdx.x == 0) off[E] = static_cast<int32_t>(S);
+  if (threadIdx.x < 64) {
+    const int e = threadIdx.x;
+    const int32_t hi = e + 1 < E ? off[e + 1] : static_cast<int32_t>(S);
+    wave_tile_offsets(e < E ? kept_rows(hi - off[e], cap) : 0, E, bm, tile_off, num_tiles);
   }
   __syncthreads();
   for (int e = threadIdx.x; e <= E; e += kScanThreads) offsets[e] = off[e];
@@ -269,16 +286,11 @@ __global__ __launch_bounds__(kScanThreads) void retile_kernel(const int32_t* __r
                                                               int32_t* __restrict__ num_tiles) {
   __shared__ int32_t tile_off[kMaxE + 1];
   __shared__ int32_t kept[kMaxE];
-  if (threadIdx.x < E) kept[threadIdx.x] = kept_rows(offsets[threadIdx.x + 1] - offsets[threadIdx.x], cap);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t nt = 0;
-    for (int e = 0; e < E; ++e) {
-      tile_off[e] = nt;
-      nt += (kept[e] + bm2 - 1) / bm2;
-    }
-    tile_off[E] = nt;
-    *num_tiles = nt;
+  if (threadIdx.x < 64) {
+    const int e = threadIdx.x;
+    const int32_t rows = e < E ? kept_rows(offsets[e + 1] - offsets[e], cap) : 0;
+    if (e < E) kept[e] = rows;
+    wave_tile_offsets(rows, E, bm2, tile_off, num_tiles);
   }
   __syncthreads();
   const int32_t nt = tile_off[E];
