@@ -33,10 +33,18 @@ __global__ __launch_bounds__(kPermThreads) void count_kernel(const int32_t* __re
   for (int e = threadIdx.x; e < E; e += kPermThreads) c[e] = 0;
   __syncthreads();
   const int64_t s0 = static_cast<int64_t>(blockIdx.x) * kSlotsPerBlock;
-  for (int i = threadIdx.x; i < kSlotsPerBlock; i += kPermThreads) {
-    const int64_t s = s0 + i;
-    if (s < S) atomicAdd(&c[idx[s]], 1);
+  // All of a thread's expert indices are loaded first (one memory latency),
+  // then counted.
+  constexpr int kPer = kSlotsPerBlock / kPermThreads;
+  int32_t ev[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int64_t s = s0 + threadIdx.x + q * kPermThreads;
+    ev[q] = s < S ? idx[s] : 0;
   }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q)
+    if (s0 + threadIdx.x + q * kPermThreads < S) atomicAdd(&c[ev[q]], 1);
   __syncthreads();
   // Expert-major layout [E][nblk]: a flat exclusive scan of it is, for
   // every (expert, block), the expert's offset plus the rows of that expert
@@ -234,11 +242,19 @@ __global__ __launch_bounds__(kPermThreads) void scatter_kernel(const int32_t* __
   __syncthreads();
   const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kSlotsPerBlock +
                      static_cast<int64_t>(wave) * kSlotsPerWave;
-  // Pass 1: per-wave counts.
-  for (int i = lane; i < kSlotsPerWave; i += 64) {
-    const int64_t s = w0 + i;
-    if (s < S) atomicAdd(&wave_cnt[wave][idx[s]], 1);
+  // Pass 1: per-wave counts. Step q of the wave covers slots w0 + 64 q +
+  // lane; the wave's expert indices are loaded once, all at a time, and kept
+  // for pass 2 (slots past S carry E).
+  constexpr int kSteps = kSlotsPerWave / 64;
+  int32_t ev[kSteps];
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int64_t s = w0 + q * 64 + lane;
+    ev[q] = s < S ? idx[s] : E;
   }
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q)
+    if (w0 + q * 64 + lane < S) atomicAdd(&wave_cnt[wave][ev[q]], 1);
   __syncthreads();
   // Per-wave running counters start at the block base plus the counts of
   // the earlier waves of the block.
@@ -254,10 +270,11 @@ __global__ __launch_bounds__(kPermThreads) void scatter_kernel(const int32_t* __
   __syncthreads();
   // Pass 2: stable ranks, 64 slots per step in flat order.
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int i0 = 0; i0 < kSlotsPerWave; i0 += 64) {
-    const int64_t s = w0 + i0 + lane;
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int64_t s = w0 + q * 64 + lane;
     const bool ok = s < S;
-    const int e = ok ? idx[s] : E;
+    const int e = ev[q];
     const uint64_t m = same_expert_mask(e);
     const int rank = __popcll(m & lt);
     const int cnt = __popcll(m);
