@@ -125,6 +125,58 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
 // (experts ascending, block_m rows each, the last partial), derived from
 // the expert offsets: under capacity routing the dropped slots still carry
 // router gradient, though no GEMM tile covers their rows.
+// k = K <= 8: lane i reads slot i's sorted row and weight, the wave
+// broadcasts them, the token's G piece is read once and all K expert-row
+// loads of a piece are issued together. Each rank's dot product still sums
+// over the pieces in order and then over the wave as in combine_bwd_kernel,
+// so the results are the same bits.
+template <typename T, int K>
+__global__ __launch_bounds__(kRowThreads) void combine_bwd_k_kernel(
+    int64_t ntok, int d, const T* __restrict__ G, const T* __restrict__ y,
+    const float* __restrict__ w, const int32_t* __restrict__ inv_perm, T* __restrict__ dY,
+    float* __restrict__ dl) {
+  constexpr int N = V16<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int my_slot = lane < K ? inv_perm[t * K + lane] : 0;
+  const float my_w = lane < K ? w[t * K + lane] : 0.0f;
+  int64_t slot[K];
+  float wi[K], dot[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    slot[i] = __builtin_amdgcn_readlane(my_slot, i);
+    wi[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), i));
+    dot[i] = 0.0f;
+  }
+  for (int c = lane * N; c < d; c += 64 * N) {
+    float g[N], yv[K][N];
+    V16<T>::load(G + t * d + c, g);
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (slot[i] >= 0) V16<T>::load_nt(y + slot[i] * d + c, yv[i]);
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+      if (slot[i] >= 0) {
+        float o[N];
+#pragma unroll
+        for (int q = 0; q < N; ++q) {
+          dot[i] = __builtin_fmaf(g[q], yv[i][q], dot[i]);
+          o[q] = wi[i] * g[q];
+        }
+        V16<T>::store(dY + slot[i] * d + c, o);
+      }
+  }
+  float my_dw = 0.0f;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const float di = wave_sum(dot[i]);
+    if (lane == i) my_dw = di;
+  }
+  const float s = wave_sum(lane < K ? my_w * my_dw : 0.0f);
+  if (lane < K) dl[t * K + lane] = my_w * (my_dw - s);
+}
+
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void router_partial_kernel(
     const T* __restrict__ x, int d, int topk, const int32_t* __restrict__ perm,
@@ -284,6 +336,65 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
       V16<T>::load_nt(dx_shared + t * d + c, v);
 #pragma unroll
       for (int q = 0; q < N; ++q) acc[q] += v[q];
+    }
+    V16<T>::store_nt(dx + t * d + c, acc);
+  }
+}
+
+// k = K <= 8: lane i reads slot i's sorted row, expert and router-logit
+// gradient (one coalesced load each), the wave broadcasts them, and all K
+// expert-row and router-row loads of a piece (and the shared row's) are
+// issued before any is used: one memory latency per token instead of 2K
+// dependent ones. Same arithmetic and order as dx_gather_kernel.
+template <typename T, int K>
+__global__ __launch_bounds__(kRowThreads) void dx_gather_k_kernel(
+    int64_t ntok, int d, const T* __restrict__ dxs, const int32_t* __restrict__ inv_perm,
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
+    const float* __restrict__ wrT, const T* __restrict__ dx_shared, T* __restrict__ dx) {
+  constexpr int N = V16<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * (kRowThreads / 64) + (threadIdx.x >> 6);
+  if (t >= ntok) return;
+  const int my_slot = lane < K ? inv_perm[t * K + lane] : 0;
+  const int my_e = lane < K ? topk_idx[t * K + lane] : 0;
+  const float my_l = lane < K ? dl[t * K + lane] : 0.0f;
+  int64_t slot[K];
+  int e[K];
+  float li[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    slot[i] = __builtin_amdgcn_readlane(my_slot, i);
+    e[i] = __builtin_amdgcn_readlane(my_e, i);
+    li[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_l), i));
+  }
+  for (int c = lane * N; c < d; c += 64 * N) {
+    float v[K][N], wv[K][N], sv[N];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (slot[i] >= 0) {
+        V16<T>::load_nt(dxs + slot[i] * d + c, v[i]);
+      } else {
+        // dropped by capacity routing: only the router term
+#pragma unroll
+        for (int q = 0; q < N; ++q) v[i][q] = 0.0f;
+      }
+#pragma unroll
+      for (int q = 0; q < N; q += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wrT + static_cast<int64_t>(e[i]) * d + c + q);
+        wv[i][q] = w4.x; wv[i][q + 1] = w4.y; wv[i][q + 2] = w4.z; wv[i][q + 3] = w4.w;
+      }
+    }
+    if (dx_shared) V16<T>::load_nt(dx_shared + t * d + c, sv);
+    float acc[N];
+#pragma unroll
+    for (int q = 0; q < N; ++q) acc[q] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += __builtin_fmaf(li[i], wv[i][q], v[i][q]);
+    if (dx_shared) {
+#pragma unroll
+      for (int q = 0; q < N; ++q) acc[q] += sv[q];
     }
     V16<T>::store_nt(dx + t * d + c, acc);
   }
@@ -475,9 +586,22 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   // is the `s` its launches use).
   auto routed_bwd = [&](hipStream_t s) {
     // a11: combine backward and per-slot router gradient
-    MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
-               dim3(kRowThreads), 0, s, T_, k, d, static_cast<const T*>(grad_out),
-               static_cast<const T*>(y_sorted), r.topk_w, r.inv_perm, dY, dl);
+    const T* g_t = static_cast<const T*>(grad_out);
+    const T* y_t = static_cast<const T*>(y_sorted);
+#define MOE_CB_K(KK)                                                                          \
+  case KK:                                                                                    \
+    MOE_LAUNCH("bwd_combine", (combine_bwd_k_kernel<T, KK>),                                  \
+               dim3(static_cast<unsigned>(row_blocks)), dim3(kRowThreads), 0, s, T_, d, g_t,  \
+               y_t, r.topk_w, r.inv_perm, dY, dl);                                            \
+    break;
+    switch (k) {
+      MOE_CB_K(1) MOE_CB_K(2) MOE_CB_K(3) MOE_CB_K(4) MOE_CB_K(5) MOE_CB_K(6) MOE_CB_K(7)
+      MOE_CB_K(8)
+      default:
+        MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
+                   dim3(kRowThreads), 0, s, T_, k, d, g_t, y_t, r.topk_w, r.inv_perm, dY, dl);
+    }
+#undef MOE_CB_K
     // a12: router weight gradient (tile partials, then a per-expert ordered sum)
     MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
                dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
@@ -611,9 +735,22 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   float* wrT = reinterpret_cast<float*>(W + L.wrT);
   MOE_LAUNCH("bwd_router_transpose", router_transpose_kernel, dim3((d + 31) / 32, (E + 31) / 32),
              dim3(256), 0, s, w.w_router, d, E, wrT);
-  MOE_LAUNCH("bwd_dx", dx_gather_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
-             dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, wrT,
-             static_cast<const T*>(dxs), static_cast<T*>(grad_x));
+  const T* dxs_t = static_cast<const T*>(dxs);
+  T* gx = static_cast<T*>(grad_x);
+#define MOE_DX_K(KK)                                                                          \
+  case KK:                                                                                    \
+    MOE_LAUNCH("bwd_dx", (dx_gather_k_kernel<T, KK>), dim3(static_cast<unsigned>(row_blocks)), \
+               dim3(kRowThreads), 0, s, T_, d, dXs, r.inv_perm, r.topk_idx, dl, wrT, dxs_t, gx); \
+    break;
+  switch (k) {
+    MOE_DX_K(1) MOE_DX_K(2) MOE_DX_K(3) MOE_DX_K(4) MOE_DX_K(5) MOE_DX_K(6) MOE_DX_K(7)
+    MOE_DX_K(8)
+    default:
+      MOE_LAUNCH("bwd_dx", dx_gather_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
+                 dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, wrT, dxs_t,
+                 gx);
+  }
+#undef MOE_DX_K
   return hipGetLastError();
 }
 
