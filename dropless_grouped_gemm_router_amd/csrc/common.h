@@ -122,6 +122,10 @@ class SideFork {
  public:
   SideFork();
   hipError_t fork(hipStream_t s);
+  // A point on the side stream (mark, after the work enqueued there so far)
+  // that s waits for (wait_mark) before the work enqueued on it next.
+  hipError_t mark();
+  hipError_t wait_mark(hipStream_t s);
   hipError_t join(hipStream_t s);
   hipStream_t side() const { return side_; }
 
@@ -129,6 +133,7 @@ class SideFork {
   std::lock_guard<std::mutex> lock_;
   int dev_ = 0;
   hipStream_t side_ = nullptr;
+  hipStream_t caller_ = nullptr;
 };
 
 // Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).

@@ -236,17 +236,30 @@ void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void
   }
 }
 
-// Routed part: pack the expert weights, gate/up GEMM with SwiGLU, down GEMM.
+// The routed experts' weights in the GEMMs' layout (workspace). Depends on
+// the weights alone, so it may run on another stream before the routing.
 template <typename T>
-void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
-                  const moe_routing& r, void* y_sorted, void* saved, void* ws, void* x_sorted,
-                  hipStream_t s) {
-  const FfnLayout L = ffn_layout(p, saved != nullptr);
+void pack_routed_t(const moe_problem& p, const moe_weights& w, void* ws, bool training,
+                   hipStream_t s) {
+  const FfnLayout L = ffn_layout(p, training);
   char* W = static_cast<char*>(ws);
-  char* SV = static_cast<char*>(saved);
   const int E = p.experts, d = p.d_model, h = p.d_hidden;
   pack<T>(w.w_gate, w.w_up, W + L.gu_packed, E, d, h, true, s);
   pack<T>(w.w_down, nullptr, W + L.down_packed, E, h, d, false, s);
+}
+
+// Routed part: pack the expert weights (unless `packed`: already enqueued,
+// possibly on another stream, and ordered before this call's GEMMs by the
+// caller), gate/up GEMM with SwiGLU, down GEMM.
+template <typename T>
+void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
+                  const moe_routing& r, void* y_sorted, void* saved, void* ws, void* x_sorted,
+                  hipStream_t s, bool packed = false) {
+  const FfnLayout L = ffn_layout(p, saved != nullptr);
+  char* W = static_cast<char*>(ws);
+  char* SV = static_cast<char*>(saved);
+  const int h = p.d_hidden;
+  if (!packed) pack_routed_t<T>(p, w, ws, saved != nullptr, s);
   T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
@@ -335,17 +348,25 @@ ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training) 
 namespace {
 
 // route -> permute -> routed FFN on s.
+// route -> permute -> routed FFN on s. With a fork, the routed weights were
+// packed on its side stream before its mark, which s waits for first.
 hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* saved, void* ws,
-                          void* x_sorted, void* permute_ws, hipStream_t s) {
+                          void* x_sorted, void* permute_ws, hipStream_t s,
+                          SideFork* fork = nullptr) {
   hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
                               r.topk_idx, r.topk_w, s);
   if (e != hipSuccess) return e;
   e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, p.capacity, r.topk_idx,
                      r.expert_offsets, r.perm, r.inv_perm, r.tiles, r.num_tiles, permute_ws, s);
   if (e != hipSuccess) return e;
-  if (p.dtype == MOE_BF16) ffn_routed_t<bf16_t>(p, x, w, r, y_sorted, saved, ws, x_sorted, s);
-  else ffn_routed_t<float>(p, x, w, r, y_sorted, saved, ws, x_sorted, s);
+  if (fork) {
+    e = fork->wait_mark(s);
+    if (e != hipSuccess) return e;
+  }
+  const bool packed = fork != nullptr;
+  if (p.dtype == MOE_BF16) ffn_routed_t<bf16_t>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, packed);
+  else ffn_routed_t<float>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, packed);
   return hipGetLastError();
 }
 
@@ -363,12 +384,19 @@ hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, con
   // weights: it runs on the side stream beside route, permute and the routed
   // FFN, and the combine waits for it.
   if (p.d_shared > 0 && !L.fused) {
+    // The routed weights are packed first on the side stream too, beside the
+    // router kernel (which leaves room on every CU for the pack kernel's
+    // workgroups); the routed GEMMs wait for that mark.
     SideFork fork;
     hipError_t e = fork.fork(s);
     if (e != hipSuccess) return e;
+    if (bf) pack_routed_t<bf16_t>(p, w, ws, saved != nullptr, fork.side());
+    else pack_routed_t<float>(p, w, ws, saved != nullptr, fork.side());
+    e = fork.mark();
+    if (e != hipSuccess) return e;
     if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
     else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
-    e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s);
+    e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s, &fork);
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess) e = fork.join(s);
     if (e != hipSuccess) return e;

@@ -51,12 +51,13 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_side_mu;
 hipStream_t g_side[kMaxDevices];
-hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices];
+hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices], g_mark[kMaxDevices];
 }  // namespace
 
 SideFork::SideFork() : lock_(g_side_mu) {}
 
 hipError_t SideFork::fork(hipStream_t s) {
+  caller_ = s;
   if (trace_on()) {
     side_ = s;
     return hipSuccess;
@@ -68,6 +69,7 @@ hipError_t SideFork::fork(hipStream_t s) {
     e = hipStreamCreateWithFlags(&g_side[dev_], hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&g_fork[dev_], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&g_join[dev_], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_mark[dev_], hipEventDisableTiming);
     if (e != hipSuccess) {
       g_side[dev_] = nullptr;
       return e;
@@ -77,6 +79,17 @@ hipError_t SideFork::fork(hipStream_t s) {
   if (e == hipSuccess) e = hipStreamWaitEvent(g_side[dev_], g_fork[dev_], 0);
   if (e == hipSuccess) side_ = g_side[dev_];
   return e;
+}
+
+hipError_t SideFork::mark() {
+  // Nothing to order when the side stream is the caller's own (timer on).
+  if (side_ == nullptr || side_ == caller_) return hipSuccess;
+  return hipEventRecord(g_mark[dev_], side_);
+}
+
+hipError_t SideFork::wait_mark(hipStream_t s) {
+  if (side_ == nullptr || side_ == caller_ || side_ == s) return hipSuccess;
+  return hipStreamWaitEvent(s, g_mark[dev_], 0);
 }
 
 hipError_t SideFork::join(hipStream_t s) {

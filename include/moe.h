@@ -36,13 +36,15 @@
  *     index passed to moe_permute, or a routing state not produced by
  *     moe_route/moe_permute for the same problem, is undefined behaviour.
  *   - No global mutable state besides the optional kernel timer below
- *     and, per device, one side stream with two events (all guarded by a
+ *     and, per device, one side stream with three events (all guarded by a
  *     lock): calls on distinct streams may run concurrently from several
  *     host threads. moe_forward and moe_bwd, when the problem has a shared
  *     expert, run the shared expert's kernels on that side stream (default
  *     priority, created on the device's first such call and kept for the
  *     process), forked from and joined back to `stream` with events, so the
- *     caller sees one stream's ordering. No device memory is allocated.
+ *     caller sees one stream's ordering; moe_forward also packs the routed
+ *     experts' weights there first, and its routed GEMMs wait for that. No
+ *     device memory is allocated.
  *   - Results are deterministic: no floating-point atomics are used, and
  *     repeated calls on the same inputs give identical bits.
  */
