@@ -111,8 +111,8 @@ int cu_count();
 // Fork onto and join back from the current device's side stream (default
 // priority, non-blocking; created on first use and kept for the process).
 // The object holds a process-wide lock from construction to destruction, so
-// concurrent callers never interleave records and waits on the shared fork
-// and join events; work enqueued on side() between fork(s) and join(s) runs
+// concurrent callers never interleave records and waits on the shared fork,
+// mark and join events; work enqueued on side() between fork(s) and join(s) runs
 // beside s, after everything enqueued on s before the fork, and s waits for
 // it from the join on.
 // Runs a call's independent part on the device's side stream. While the
