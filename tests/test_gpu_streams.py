@@ -60,6 +60,34 @@ def test_concurrent_host_threads_match_lone_calls():
         assert bits_equal(ref, buf.out)
 
 
+def test_back_to_back_forwards_use_their_own_weights():
+    """moe_forward packs the routed weights into the workspace on the side
+    stream, and the routed GEMMs wait for that. Calls in a row on one stream
+    and one workspace, alternating two weight sets with no synchronisation
+    in between, must each give the bits of a lone call with their weights:
+    a call's pack may neither overtake the previous call's GEMMs nor be
+    overtaken by its own."""
+    import torch
+    p = Problem(3000, 16, 4, 256, 128, 256, "bf16", 256)
+    cases = [Case(p, seed=31), Case(p, seed=32)]
+    refs = []
+    for c in cases:
+        buf = B.allocate(p, dispatch="gather")
+        B.forward_dispatch(p, "gather", c.dev["x"], c.weights(), buf)
+        torch.cuda.synchronize()
+        refs.append(buf.out.clone())
+    assert not bits_equal(refs[0], refs[1])
+    buf = B.allocate(p, dispatch="gather")
+    outs = []
+    for i in range(6):
+        c = cases[i % 2]
+        B.forward_dispatch(p, "gather", c.dev["x"], c.weights(), buf)
+        outs.append(buf.out.clone())  # the current stream, after the call
+    torch.cuda.synchronize()
+    for i, o in enumerate(outs):
+        assert bits_equal(refs[i % 2], o), f"call {i}"
+
+
 def test_train_step_replays_from_a_hip_graph():
     """Forward (with saved activations) and backward captured once, replayed
     on new token values; every replay equals the eager step bit for bit."""
