@@ -438,7 +438,7 @@ def main():
             print(json.dumps(line), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
+        print(f"bench.py measures one GPU: libmoe has no multi-GPU path (--gpus {args.gpus} "
               "requested); the design notes describe how the path would shard.", file=sys.stderr)
         sys.exit(2)
 
