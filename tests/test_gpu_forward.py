@@ -186,6 +186,21 @@ def test_route_zero_router(p):
     assert np.array_equal(g["topk_idx"], idx)
 
 
+def test_permute_scan_long_chunks():
+    """More than 16384 (expert, block) counts: each thread of the one-workgroup
+    scan takes a chunk longer than its sixteen-entry register batch (the
+    scan's third path). Routing and the permutation bit-exact."""
+    import torch
+    from dropless_grouped_gemm_router_amd import binding as B
+    p = Problem(139264, 64, 8, 128, 64, 0, "bf16", 128)  # 272 blocks x 64 experts
+    note(f"long scan chunks: {p}")
+    c = Case(p, seed=7)
+    B.moe_route(p, c.dev["x"], c.dev["w_router"], c.buf.routing)
+    B.moe_permute(p, c.buf.routing, c.buf.workspace)
+    torch.cuda.synchronize()
+    check_routing(c)
+
+
 def test_skewed_routing_empty_experts():
     """A router that sends every token to experts 0 and 1: two experts with
     every slot (many tiles each), the rest empty."""
