@@ -64,6 +64,9 @@ SMALL = [
     Problem(517, 16, 4, 256, 128, 128, "fp32", 32, capacity=100),
     Problem(2000, 64, 8, 256, 128, 128, "bf16", 128, skew=0.9, capacity=200),
     Problem(300, 8, 2, 256, 128, 0, "bf16", 64, capacity=1),
+    # odd top_k for the k-specialised gathers (combine backward, dx)
+    Problem(400, 6, 3, 128, 128, 0, "bf16", 64, capacity=150),
+    Problem(300, 12, 7, 128, 128, 128, "fp32", 64),
 ]
 
 
