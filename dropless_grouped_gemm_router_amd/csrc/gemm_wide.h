@@ -59,13 +59,17 @@ __device__ __forceinline__ void wide_barrier() { asm volatile("s_barrier" ::: "m
 // tile row r = (4 w + i) * 8 + l / 8, 16-byte position l % 8 of LDS row r
 // (and of row 256 + r for B); the lane's global addresses already point at
 // the chunk that belongs at that position.
+// With with_b false only the A rows are loaded: the B rows of the stage
+// are already in the buffer (the same weights as the previous item's).
 __device__ __forceinline__ void wide_issue(char* buf, const char* const (&a_row)[kWideLoads],
                                            const char* b_base, const int (&b_off)[2],
-                                           int64_t b_step, int koff, int wave) {
+                                           int64_t b_step, int koff, int wave,
+                                           bool with_b = true) {
 #pragma unroll
   for (int i = 0; i < kWideLoads; ++i)
     __builtin_amdgcn_global_load_lds(a_row[i] + koff, buf + (wave * kWideLoads + i) * 1024, 16, 0,
                                      0);
+  if (!with_b) return;
 #pragma unroll
   for (int i = 0; i < kWideLoads; ++i)
     __builtin_amdgcn_global_load_lds(b_base + koff + b_off[i & 1] + i * b_step,
@@ -201,6 +205,34 @@ __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int6
       : "memory");
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
+    const int r = k * 8 + (lane >> 3);
+    *reinterpret_cast<u32x4*>(dst + min(r, rows - 1) * ld + c * 8) = v[k];
+  }
+}
+
+// wide_drain for a 32-row block (region rows 0..31, four stores per lane;
+// rows >= rows are written over the tile's last row as in wide_drain).
+__device__ __forceinline__ void wide_drain32(const char* region, bf16_t* dst, int64_t ld, int rows,
+                                             int lane) {
+  const int c = lane & 7;
+  uint32_t ad[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int r = k * 8 + (lane >> 3);
+    ad[k] = lds_addr(region + r * 128 + ((c ^ (r & 7)) << 4));
+  }
+  u32x4 v[4];
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
     const int r = k * 8 + (lane >> 3);
     *reinterpret_cast<u32x4*>(dst + min(r, rows - 1) * ld + c * 8) = v[k];
   }
@@ -391,22 +423,25 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
       wide_drain_swiglu_bwd(p, region, orow, nt * WideCfg::BN + wn * 128 + h * 32, wrows, lane);
     }
   } else if (kEpi == kEpiStore) {
-    // Two passes of 64 columns (MFMA tiles j = 2h, 2h + 1).
+    // Four passes of 32 rows x 64 columns (MFMA tile row i, tiles j = 2h,
+    // 2h + 1) through the first 4 KiB of the region: the wave's 4 KiB share
+    // of the buffer's A half, so a stage buffer's B half survives the
+    // epilogue (wide_gemm_kernel keeps the weights of K = 128 GEMMs).
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const f32x16_t& a = acc[i][2 * h + jj];
-            wide_park(region, i * 32 + r32, jj * 64 + rr * 16 + g * 8, a[4 * rr], a[4 * rr + 1],
+            wide_park(region, r32, jj * 64 + rr * 16 + g * 8, a[4 * rr], a[4 * rr + 1],
                       a[4 * rr + 2], a[4 * rr + 3]);
           }
-      const int col = nt * WideCfg::BN + wn * 128 + h * 64;
-      wide_drain(region, c + orow * p.ldc + col, p.ldc, wrows, lane);
-    }
+        const int col = nt * WideCfg::BN + wn * 128 + h * 64;
+        wide_drain32(region, c + (orow + i * 32) * p.ldc + col, p.ldc, wrows - i * 32, lane);
+      }
   } else {
     const int hcol = nt * (WideCfg::BN / 2) + wn * 64;
     wide_park_swiglu<0>(acc, region, g, r32);
@@ -496,6 +531,13 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
   int buf = 0;
   wide_issue(smem, a_cur, b1_cur, b_off, b_step, 0, wave);
   int stores_out = 0;  // stores the previous item's epilogue left in flight
+  // K = 128 plain-store GEMMs (the routed down projection): each stage
+  // always lands in the same buffer, so when the next item has the same
+  // weights (same group and N tile, as a workgroup's consecutive items
+  // mostly do) only its A rows are loaded; the epilogue parks in the A half.
+  const bool keep_b = kEpi == kEpiStore && nk == 2 && p.b2 == nullptr;
+  bool b_same = false;       // this item's B rows are already in the buffers
+  bool b_same_next = false;  // the same for the next item
 
   while (true) {
     const int nt = w % n_tiles_n;
@@ -523,11 +565,12 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
       }
       if (s + 1 < nk) {
         wide_issue(nb, a_cur, (s + 1) < ks_split ? b1_cur : b2_cur, b_off, b_step, (s + 1) * 128,
-                   wave);
+                   wave, !b_same);
       } else if (nxt.rows > 0) {
+        b_same_next = keep_b && nxt.group == cur.group && w1 % n_tiles_n == nt;
         wide_a_rows<kGather>(p, src, chunk_off, a_cur);
         wide_b_bases(p, nxt, w1 % n_tiles_n, ldb, b1_cur, b2_cur);
-        wide_issue(nb, a_cur, b1_cur, b_off, b_step, 0, wave);
+        wide_issue(nb, a_cur, b1_cur, b_off, b_step, 0, wave, !b_same_next);
       }
       if (s == 0 && nk > 1) {
         nxt = (w1 < w_end) ? wide_tile<kDense>(p, tiles, num_tiles, w1, n_tiles_n) : TileInfo{0, 0, 0};
@@ -543,7 +586,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
     // The buffer of the last stage is free once every wave is done with it
     // (the other one is receiving the next item's first stage).
     wide_barrier();
-    wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * 8192,
+    wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * (kEpi == kEpiStore ? 4096 : 8192),
                         kEpi == kEpiCombine ? smem + 2 * kWideStage + wave * 4096 : nullptr,
                         cur.row0, cur.rows, nt, wm, wn, g, r32, lane);
     stores_out = wide_epilogue_stores<kEpi>(p);
@@ -551,6 +594,7 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
     if (nxt.rows <= 0) break;
     w = w1;
     cur = nxt;
+    b_same = b_same_next;
   }
 }
 
