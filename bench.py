@@ -269,6 +269,31 @@ def time_steps(step, steps, warmup):
     return start.elapsed_time(stop) / steps
 
 
+def pages_timing(step, ms_hint, samples=21):
+    """The pages' timing protocol (kernel_gmm_gpu.json result records, fields
+    median_ms, q1_ms, q3_ms and inner): samples of `inner` back-to-back
+    steps, inner = clamp(round(45 ms / t), 1, 200) for a step time t, each
+    sample bracketed by HIP events on the current stream; milliseconds per
+    step of the median sample and of the quartiles."""
+    import statistics
+
+    import torch
+
+    inner = max(1, min(200, round(45.0 / max(ms_hint, 1e-3))))
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(samples + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(samples):
+        for _ in range(inner):
+            step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) / inner for i in range(samples))
+    q = statistics.quantiles(per, n=4, method="inclusive")
+    return {"samples": samples, "inner": inner, "median_ms": statistics.median(per),
+            "q1_ms": q[0], "q3_ms": q[2], "min_ms": per[0], "max_ms": per[-1]}
+
+
 def train_step_line(B, steps, warmup, tokens=0):
     """Forward + backward on the train-step workload (16384 tokens, or
     `tokens` of the same layer)."""
@@ -292,6 +317,7 @@ def train_step_line(B, steps, warmup, tokens=0):
         B.backward(p, x, dev, g, buf)
 
     ms = time_steps(step, steps, warmup)
+    pages = pages_timing(step, ms)
     # per-kernel times of the same steps, from libmoe's HIP events (with the
     # kernel timer on, the shared expert's kernels run on the caller's
     # stream, so each duration is that of the kernel alone)
@@ -306,6 +332,7 @@ def train_step_line(B, steps, warmup, tokens=0):
     avg = {kn: v["ms"] / v["count"] for kn, v in kern.items()}
     roofs = {kn: roofline_of(kn, wk[kn][0], wk[kn][1], avg[kn], p.dtype) for kn in wk if kn in avg}
     return {"workload": name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+            "pages_timing": pages,
             "tflops_3x_fwd": 3 * fwd / (ms * 1e-3) / 1e12, "steps": steps, "warmup": warmup,
             "kernels_ms_per_step": {kn: round(v["ms"] / steps, 5) for kn, v in sorted(kern.items())},
             "kernel_rooflines": {kn: {"frac": round(r["frac"], 4), "achieved": round(r["achieved"], 1),
@@ -500,6 +527,8 @@ def main():
         torch.cuda.synchronize()
     print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
     ms = time_steps(timed, args.steps, 0)
+    print("bench: pages' timing protocol", file=sys.stderr, flush=True)
+    pages = pages_timing(timed, ms)
     # Per-kernel times: libmoe's HIP events bracket every launch. In the
     # timed steps the shared expert runs beside the routed path on a second
     # stream, so kernel durations there include time shared with other
@@ -550,6 +579,7 @@ def main():
                    "block_m": p.block_m, "skew": p.skew, "dispatch": args.dispatch,
                    "routing": "capacity" if p.capacity else "dropless", "capacity": p.capacity,
                    "hip_graph": bool(args.graph)},
+        "pages_timing": dict(pages, tokens_per_s_median=p.tokens / (pages["median_ms"] * 1e-3)),
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
         "roofline": roof,

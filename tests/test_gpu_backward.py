@@ -120,3 +120,72 @@ def test_train_workload_full_size():
     c = Case(p, seed=0, training=True)
     gx, g = run_bwd(c)
     check_grads(c, gx, g)
+
+
+def test_backward_maxtok_shape_elementwise():
+    """The max-token train-step shape (kernel_gmm_gpu.json "maxtok" suite:
+    E=8, top-2, d_model 512, d_hidden 1024, bf16) at 3000 tokens: every
+    element of every gradient and of dx against the oracle."""
+    p = Problem(3000, 8, 2, 512, 1024, 0, "bf16", 128)
+    note(f"backward maxtok shape {p}")
+    c = Case(p, seed=13, training=True)
+    gx, g = run_bwd(c)
+    check_grads(c, gx, g)
+
+
+LARGE_TOKENS = 2228224  # T*k*d_model = 2,281,701,376 > 2^31 elements per slot buffer
+
+
+@pytest.mark.timeout(900)
+def test_train_step_past_2e31_elements_sampled():
+    """The max-token shape at 2,228,224 tokens: y_sorted, dY and the per-slot
+    dX hold more than 2^31 elements and the saved gate/up activations more
+    than 2^33, so every slot-indexed address needs 64 bits. Routing and the
+    permutation bit-exact on every token; out and dx on sampled tokens,
+    among them tokens whose slots sit at the far end of the sorted rows.
+    Tokens are generated in full; grad_out is a seeded 131072-token block
+    repeated (it is indexed by token, below 2^31 elements)."""
+    import dataclasses
+
+    import torch
+
+    from dropless_grouped_gemm_router_amd.inputs import Tensor, make_inputs
+
+    p = Problem(LARGE_TOKENS, 8, 2, 512, 1024, 0, "bf16", 128)
+    note(f"train step past 2^31 elements: {p}: generating inputs")
+    inp = make_inputs(p, seed=0)
+    blk = make_inputs(dataclasses.replace(p, tokens=131072), seed=0, with_grad_out=True,
+                      names=["grad_out"])["grad_out"]
+    reps = -(-p.tokens // 131072)
+    inp["grad_out"] = Tensor(stored=np.tile(blk.stored, (reps, 1))[:p.tokens],
+                             value=np.tile(blk.value, (reps, 1))[:p.tokens])
+    c = Case(p, training=True, inputs=inp)
+    note("forward + backward on the GPU")
+    gx, g = run_bwd(c)
+    note("oracle routing of every token")
+    v = c.v
+    _, idx, w = oracle.route(v["x"], v["w_router"], p.top_k)
+    got = c.routing_np()
+    assert np.array_equal(got["topk_idx"], idx)
+    assert np.max(np.abs(got["topk_w"] - w)) < 2e-6
+    r = oracle.permute(idx, p.experts, p.block_m)
+    assert np.array_equal(got["offsets"], r["offsets"])
+    assert np.array_equal(got["perm"], r["perm"])
+    assert np.array_equal(got["inv_perm"], r["inv_perm"])
+    assert got["num_tiles"] == r["num_tiles"] and np.array_equal(got["tiles"], r["tiles"])
+    S = p.tokens * p.top_k
+    far = r["perm"][[S - 1, S - 2, S - 777, S // 2 + 5, (1 << 31) // p.d_model + 3]] // p.top_k
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([[0, p.tokens - 1], far,
+                                     rng.choice(p.tokens, 120, replace=False)]))
+    note(f"oracle on {rows.size} sampled tokens")
+    ref = oracle.forward_rows(v["x"], v["w_gate"], v["w_up"], v["w_down"], idx, w, rows=rows)
+    err = oracle.rel_err(to_np(c.buf.out[rows.tolist()]), ref)
+    # dx of a token depends on that token alone (dropless): the oracle's
+    # backward over the sampled tokens gives their rows exactly
+    gref = oracle.backward(v["x"][rows], v["w_router"], v["w_gate"], v["w_up"], v["w_down"],
+                           v["grad_out"][rows], idx[rows], w[rows])
+    ex = oracle.rel_err(to_np(gx[rows.tolist()]), gref["x"])
+    note(f"out rel err {err:.3e}, dx rel err {ex:.3e}")
+    assert err < TOL[p.dtype] and ex < TOL[p.dtype]
+    assert bool(torch.isfinite(g["w_gate"]).all()) and bool(torch.isfinite(g["w_down"]).all())

@@ -78,8 +78,14 @@ def test_dispatch_matches_staged_and_oracle(p, dispatch):
     n_tiles = int(c.buf.routing["num_tiles"].cpu().item())
     got = run_variant(c, dispatch)
     assert_same_forward(c.buf, got, n_tiles)
-    idx = got.routing["topk_idx"].cpu().numpy()
-    w = got.routing["topk_w"].cpu().numpy().astype(np.float64)
+    # routing from the oracle, not from the device: indices bit-exact,
+    # weights to fp32 rounding, the output from the oracle's own routing
+    _, idx, w = oracle.route(c.v["x"], c.v["w_router"], p.top_k)
+    assert np.array_equal(got.routing["topk_idx"].cpu().numpy(), idx)
+    assert np.max(np.abs(got.routing["topk_w"].cpu().numpy() - w)) < 2e-6
+    r = oracle.permute(idx, p.experts, p.block_m, capacity=p.capacity)
+    assert np.array_equal(got.routing["perm"].cpu().numpy(), r["perm"])
+    assert np.array_equal(got.routing["inv_perm"].cpu().numpy(), r["inv_perm"])
     ref = oracle.forward_rows(c.v["x"], c.v["w_gate"], c.v["w_up"], c.v["w_down"], idx, w,
                               *c.shared(), keep=keep_of(p, idx))
     assert oracle.rel_err(to_np(got.out), ref) < TOL[p.dtype]
@@ -126,8 +132,8 @@ def test_dispatch_full_size_workload():
         got = run_variant(c, dispatch)
         assert_same_forward(c.buf, got, n_tiles)
         if dispatch == "fused_gsum":
-            idx = got.routing["topk_idx"].cpu().numpy()
-            w = got.routing["topk_w"].cpu().numpy().astype(np.float64)
+            _, idx, w = oracle.route(c.v["x"], c.v["w_router"], p.top_k)
+            assert np.array_equal(got.routing["topk_idx"].cpu().numpy(), idx)
             rng = np.random.default_rng(5)
             rows = np.unique(np.concatenate([[0, p.tokens - 1],
                                              rng.choice(p.tokens, 126, replace=False)]))
