@@ -18,6 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_TOO_LARGE = -5
 MOE_FP32, MOE_BF16 = 0, 1
 DTYPES = {"fp32": MOE_FP32, "bf16": MOE_BF16}
 MOE_DISPATCH_GATHER, MOE_DISPATCH_SORTED, MOE_DISPATCH_FUSED_GSUM = 0, 1, 2
@@ -55,7 +56,7 @@ class moe_grads(ctypes.Structure):
 
 EXPORTED = ["moe_version", "moe_status_string", "moe_check_problem", "moe_max_tiles",
             "moe_param_count", "moe_workspace_bytes", "moe_saved_bytes", "moe_route",
-            "moe_permute", "moe_ffn_fwd", "moe_combine", "moe_forward_workspace_bytes",
+            "moe_permute", "moe_permute_static", "moe_ffn_fwd", "moe_combine", "moe_forward_workspace_bytes",
             "moe_forward", "moe_bwd", "moe_trace_enable", "moe_trace_summary"]
 
 _lib = None
@@ -81,6 +82,7 @@ def load(path: str = LIB_PATH):
         "moe_saved_bytes": (ctypes.c_size_t, [PP]),
         "moe_route": (ctypes.c_int, [PP, P, P, ctypes.POINTER(moe_routing), P]),
         "moe_permute": (ctypes.c_int, [PP, ctypes.POINTER(moe_routing), P, ctypes.c_size_t, P]),
+        "moe_permute_static": (ctypes.c_int, [PP, ctypes.POINTER(moe_routing), P]),
         "moe_ffn_fwd": (ctypes.c_int, [PP, P, ctypes.POINTER(moe_weights),
                                        ctypes.POINTER(moe_routing), P, P, P, P, ctypes.c_size_t, P]),
         "moe_combine": (ctypes.c_int, [PP, P, ctypes.POINTER(moe_routing), P, P, P]),
@@ -188,6 +190,12 @@ def moe_permute(p, routing: Dict, workspace, workspace_bytes: Optional[int] = No
     nb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     _check(load().moe_permute(ctypes.byref(problem_struct(p)), ctypes.byref(r), _ptr(workspace),
                               nb, _stream(stream)), "moe_permute")
+
+
+def moe_permute_static(p, routing: Dict, stream=None):
+    r = routing_struct(routing)
+    _check(load().moe_permute_static(ctypes.byref(problem_struct(p)), ctypes.byref(r),
+                                     _stream(stream)), "moe_permute_static")
 
 
 def moe_ffn_fwd(p, x, weights: Dict, routing: Dict, y_sorted, shared_out, saved, workspace,

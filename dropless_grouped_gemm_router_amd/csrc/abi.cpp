@@ -51,6 +51,7 @@ MOE_EXPORT const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported problem";
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_TOO_LARGE: return "problem exceeds the fixed scratch of the allocation-free entry point";
     default: return "unknown status";
   }
 }
@@ -108,6 +109,24 @@ MOE_EXPORT int moe_permute(const moe_problem* p, moe_routing* r, void* workspace
                                         p->capacity, r->topk_idx,
                                         r->expert_offsets, r->perm, r->inv_perm, r->tiles,
                                         r->num_tiles, workspace, as_stream(stream)));
+}
+
+MOE_EXPORT int moe_permute_static(const moe_problem* p, moe_routing* r, void* stream) {
+  int st = check(p);
+  if (st != MOE_OK) return st;
+  if (p->tokens == 0) return MOE_OK;
+  if (!r || !ok_ptr(r->topk_idx, 4) || !ok_ptr(r->expert_offsets, 4) || !ok_ptr(r->perm, 4) ||
+      !ok_ptr(r->inv_perm, 4) || !ok_ptr(r->tiles, 4) || !ok_ptr(r->num_tiles, 4))
+    return MOE_ERR_INVALID;
+  if (moe::permute_ws_bytes(p->tokens * p->top_k, p->experts) > moe::static_scratch_bytes())
+    return MOE_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  const hipError_t e = moe::static_scratch(&scratch);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_permute(p->tokens, p->top_k, p->experts, p->block_m,
+                                        p->capacity, r->topk_idx, r->expert_offsets, r->perm,
+                                        r->inv_perm, r->tiles, r->num_tiles, scratch,
+                                        as_stream(stream)));
 }
 
 MOE_EXPORT int moe_ffn_fwd(const moe_problem* p, const void* x, const moe_weights* w,

@@ -156,6 +156,11 @@ hipError_t launch_route(int dtype, const void* x, const float* w_router, int64_t
                         int k, int32_t* topk_idx, float* topk_w, hipStream_t s);
 
 size_t permute_ws_bytes(int64_t S, int E);
+// The fixed device scratch of the allocation-free permute (moe_permute_static):
+// its size, and its address on the current device (looked up on the first
+// call per device).
+size_t static_scratch_bytes();
+hipError_t static_scratch(void** out);
 hipError_t launch_permute(int64_t T, int k, int E, int bm, int cap, const int32_t* topk_idx,
                           int32_t* offsets, int32_t* perm, int32_t* inv_perm, int32_t* tiles,
                           int32_t* num_tiles, void* ws, hipStream_t s);

@@ -335,6 +335,40 @@ hipError_t launch_retile(const int32_t* offsets, int E, int bm2, int cap, int32_
   return hipPeekAtLastError();
 }
 
+// Scratch of moe_permute_static: the per-block expert counts live in this
+// fixed device array instead of a caller workspace. Each device holds its
+// own copy at its own address, looked up once per device with
+// hipGetSymbolAddress (the array's name is not a device address in host
+// code). The count kernel writes every entry the scan and scatter read, so
+// nothing needs clearing between calls; calls on one device share it.
+constexpr size_t kStaticScratchBytes = size_t{1} << 20;
+static __device__ __align__(256) int32_t scratch[kStaticScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+}  // namespace
+
+size_t static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
 size_t permute_ws_bytes(int64_t S, int E) {
   const int64_t nblk = (S + kSlotsPerBlock - 1) / kSlotsPerBlock;
   return align_up(sizeof(int32_t) * static_cast<size_t>(nblk) * E, 256);

@@ -63,7 +63,8 @@ typedef enum {
   MOE_ERR_INVALID = -1,     /* null pointer, bad size, misaligned pointer */
   MOE_ERR_UNSUPPORTED = -2, /* valid problem outside what the kernels implement */
   MOE_ERR_WORKSPACE = -3,   /* workspace smaller than moe_workspace_bytes() */
-  MOE_ERR_HIP = -4          /* a kernel launch failed */
+  MOE_ERR_HIP = -4,         /* a kernel launch failed */
+  MOE_ERR_TOO_LARGE = -5    /* beyond the fixed scratch of moe_permute_static */
 } moe_status;
 
 typedef enum { MOE_FP32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -213,6 +214,22 @@ int moe_route(const moe_problem* p, const void* x, const float* w_router, moe_ro
  */
 int moe_permute(const moe_problem* p, moe_routing* r, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, results and errors as moe_permute,
+ * except that its scratch (the per-block expert counts) lives in a fixed
+ * 1 MiB device array that libmoe holds on each GPU it runs on until the
+ * process ends: experts * ceil(tokens * top_k / 4096) * 4 bytes must fit
+ * in it (up to 16,777,216 token-slots at 64 experts), else
+ * MOE_ERR_TOO_LARGE and nothing is enqueued. It allocates nothing (the
+ * array's device address is looked up once per device, on the first call
+ * there). Every call on one GPU uses that GPU's one array: calls that can
+ * overlap on one GPU (different streams, or several host threads) race and
+ * must be ordered by the caller. The array needs no clearing between calls.
+ */
+int moe_permute_static(const moe_problem* p, moe_routing* r, void* stream);
 
 /*
  * Stage "experts_grouped_swiglu" (kernel_gmm_gpu.json "pieces" suite):

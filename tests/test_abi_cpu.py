@@ -25,7 +25,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = B.load()
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(B.EXPORTED) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -124,6 +124,24 @@ def test_permute_argument_errors():
     expect(B.MOE_ERR_INVALID, B.moe_permute, P, dict(r, perm=None), ws, workspace_bytes=need,
            stream=0)
     B.moe_permute(Problem(0, 8, 2, 256, 128, 0, "bf16", 64), {}, None, workspace_bytes=0, stream=0)
+
+
+def test_permute_static_argument_errors():
+    """The allocation-free permute checks everything on the host before it
+    touches the device: bad pointers, and problems whose per-block counts
+    would not fit its fixed 1 MiB scratch (64 experts x ceil(S / 4096)
+    blocks x 4 bytes)."""
+    r = fake_routing()
+    expect(B.MOE_ERR_INVALID, B.moe_permute_static, P, dict(r, inv_perm=None), stream=0)
+    expect(B.MOE_ERR_INVALID, B.moe_permute_static, P, dict(r, tiles=FakeTensor(0x40000002)),
+           stream=0)
+    # 64 experts: 4096 blocks of 4096 slots fit, one more does not
+    fits = Problem((1 << 24) // 8, 64, 8, 128, 64, 0, "bf16", 256)
+    over = Problem((1 << 24) // 8 + 1, 64, 8, 128, 64, 0, "bf16", 256)
+    assert fits.tokens * fits.top_k == 4096 * 4096
+    expect(B.MOE_ERR_TOO_LARGE, B.moe_permute_static, over, r, stream=0)
+    assert "fixed scratch" in B.status_string(B.MOE_ERR_TOO_LARGE)
+    B.moe_permute_static(Problem(0, 8, 2, 256, 128, 0, "bf16", 64), {}, stream=0)
 
 
 def test_ffn_and_combine_argument_errors():
