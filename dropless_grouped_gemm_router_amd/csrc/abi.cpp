@@ -30,7 +30,9 @@ int check(const moe_problem* p) {
   if (p->experts > 64) return MOE_ERR_UNSUPPORTED;
   if (p->d_model % 128 != 0 || p->d_model > 8192) return MOE_ERR_UNSUPPORTED;
   if (p->d_hidden % 64 != 0 || p->d_shared % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (p->tokens * static_cast<int64_t>(p->top_k) >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED;
+  // tokens * top_k < 2^31, tested without forming the product (tokens may be
+  // anywhere up to INT64_MAX)
+  if (p->tokens > ((int64_t{1} << 31) - 1) / p->top_k) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -58,6 +58,9 @@ def test_param_count_and_tiles():
     (dict(d_hidden=100), B.MOE_ERR_UNSUPPORTED),
     (dict(d_shared=96), B.MOE_ERR_UNSUPPORTED),
     (dict(tokens=1 << 30, top_k=2), B.MOE_ERR_UNSUPPORTED),
+    # tokens * top_k would overflow int64: rejected without forming it
+    (dict(tokens=(1 << 62) + 1, top_k=8), B.MOE_ERR_UNSUPPORTED),
+    (dict(tokens=(1 << 31) // 2 - 1, top_k=2), B.MOE_OK),
     (dict(), B.MOE_OK),
     (dict(tokens=0), B.MOE_OK),
 ])
