@@ -89,9 +89,10 @@ def load(path: str = LIB_PATH):
         "moe_forward_workspace_bytes": (ctypes.c_size_t, [PP, ctypes.c_int, ctypes.c_int]),
         "moe_forward": (ctypes.c_int, [PP, ctypes.c_int, P, ctypes.POINTER(moe_weights),
                                        ctypes.POINTER(moe_routing), P, P, P, P, ctypes.c_size_t,
-                                       P]),
+                                       P, P]),
         "moe_bwd": (ctypes.c_int, [PP, P, ctypes.POINTER(moe_weights), ctypes.POINTER(moe_routing),
-                                   P, P, P, P, ctypes.POINTER(moe_grads), P, ctypes.c_size_t, P]),
+                                   P, P, P, P, ctypes.POINTER(moe_grads), P, ctypes.c_size_t, P,
+                                   P]),
         "moe_trace_enable": (ctypes.c_int, [ctypes.c_int]),
         "moe_trace_summary": (ctypes.c_int, [ctypes.c_char_p, ctypes.c_size_t]),
     }
@@ -120,6 +121,15 @@ def _stream(stream) -> Optional[int]:
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
+
+
+def _side(side_stream) -> Optional[int]:
+    """The optional second stream: None stays NULL (no second stream)."""
+    if side_stream is None:
+        return None
+    if isinstance(side_stream, int):
+        return side_stream
+    return side_stream.cuda_stream
 
 
 def problem_struct(p) -> moe_problem:
@@ -223,21 +233,23 @@ def moe_forward_workspace_bytes(p, dispatch, training: bool = False) -> int:
 
 
 def moe_forward(p, dispatch, x, weights: Dict, routing: Dict, y_sorted, saved, out, workspace,
-                workspace_bytes: Optional[int] = None, stream=None):
+                workspace_bytes: Optional[int] = None, stream=None, side_stream=None):
     w, r = weights_struct(weights), routing_struct(routing)
     nb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     _check(load().moe_forward(ctypes.byref(problem_struct(p)), _dispatch(dispatch), _ptr(x),
                               ctypes.byref(w), ctypes.byref(r), _ptr(y_sorted), _ptr(saved),
-                              _ptr(out), _ptr(workspace), nb, _stream(stream)), "moe_forward")
+                              _ptr(out), _ptr(workspace), nb, _stream(stream), _side(side_stream)),
+           "moe_forward")
 
 
 def moe_bwd(p, x, weights: Dict, routing: Dict, y_sorted, saved, grad_out, grad_x, grads: Dict,
-            workspace, workspace_bytes: Optional[int] = None, stream=None):
+            workspace, workspace_bytes: Optional[int] = None, stream=None, side_stream=None):
     w, r, g = weights_struct(weights), routing_struct(routing), grads_struct(grads)
     nb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
     _check(load().moe_bwd(ctypes.byref(problem_struct(p)), _ptr(x), ctypes.byref(w),
                           ctypes.byref(r), _ptr(y_sorted), _ptr(saved), _ptr(grad_out),
-                          _ptr(grad_x), ctypes.byref(g), _ptr(workspace), nb, _stream(stream)),
+                          _ptr(grad_x), ctypes.byref(g), _ptr(workspace), nb, _stream(stream),
+                          _side(side_stream)),
            "moe_bwd")
 
 
@@ -323,18 +335,19 @@ def forward(p, x, weights: Dict, buf: Buffers, training: bool = False, stream=No
 
 
 def forward_dispatch(p, dispatch, x, weights: Dict, buf: Buffers, training: bool = False,
-                     stream=None):
+                     stream=None, side_stream=None):
     """The whole forward in one moe_forward call with a dispatch variant
     (buf from ``allocate(..., dispatch=...)``); returns buf.out."""
     moe_forward(p, dispatch, x, weights, buf.routing, buf.y_sorted,
-                buf.saved if training else None, buf.out, buf.workspace, stream=stream)
+                buf.saved if training else None, buf.out, buf.workspace, stream=stream,
+                side_stream=side_stream)
     return buf.out
 
 
-def backward(p, x, weights: Dict, grad_out, buf: Buffers, stream=None):
+def backward(p, x, weights: Dict, grad_out, buf: Buffers, stream=None, side_stream=None):
     """Gradients of sum(out * grad_out) after forward(..., training=True)."""
     moe_bwd(p, x, weights, buf.routing, buf.y_sorted, buf.saved, grad_out, buf.grad_x, buf.grads,
-            buf.workspace, stream=stream)
+            buf.workspace, stream=stream, side_stream=side_stream)
     return buf.grad_x, buf.grads
 
 

@@ -171,7 +171,7 @@ MOE_EXPORT size_t moe_forward_workspace_bytes(const moe_problem* p, int dispatch
 
 MOE_EXPORT int moe_forward(const moe_problem* p, int dispatch, const void* x, const moe_weights* w,
                            moe_routing* r, void* y_sorted, void* saved, void* out, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, void* stream, void* side_stream) {
   if (dispatch < MOE_DISPATCH_GATHER || dispatch > MOE_DISPATCH_FUSED_GSUM) return MOE_ERR_INVALID;
   int st = check(p);
   if (st != MOE_OK) return st;
@@ -188,13 +188,13 @@ MOE_EXPORT int moe_forward(const moe_problem* p, int dispatch, const void* x, co
   if (workspace_bytes < moe::forward_layout(*p, dispatch, saved != nullptr).total)
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_forward(*p, dispatch, x, *w, *r, y_sorted, saved, out, workspace,
-                                        as_stream(stream)));
+                                        as_stream(stream), as_stream(side_stream)));
 }
 
 MOE_EXPORT int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w,
                        const moe_routing* r, const void* y_sorted, const void* saved,
                        const void* grad_out, void* grad_x, const moe_grads* g, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, void* stream, void* side_stream) {
   int st = check(p);
   if (st != MOE_OK) return st;
   // The backward GEMMs tile the hidden widths by 128.
@@ -209,7 +209,7 @@ MOE_EXPORT int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w
     // (zero) and fully overwritten.
     return hip_status(moe::launch_bwd(*p, x, w ? *w : moe_weights{}, r ? *r : moe_routing{},
                                       y_sorted, saved, grad_out, grad_x, *g, workspace,
-                                      as_stream(stream)));
+                                      as_stream(stream), nullptr));
   }
   if (!w || !r || !ok_ptr(x) || !ok_ptr(w->w_router, 4) || !ok_ptr(w->w_gate) || !ok_ptr(w->w_up) ||
       !ok_ptr(w->w_down) || !ok_ptr(r->topk_idx, 4) || !ok_ptr(r->topk_w, 4) ||
@@ -223,5 +223,5 @@ MOE_EXPORT int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w
     return MOE_ERR_INVALID;
   if (workspace_bytes < moe::bwd_ws_bytes(*p)) return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_bwd(*p, x, *w, *r, y_sorted, saved, grad_out, grad_x, *g,
-                                    workspace, as_stream(stream)));
+                                    workspace, as_stream(stream), as_stream(side_stream)));
 }

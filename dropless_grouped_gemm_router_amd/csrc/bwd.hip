@@ -560,7 +560,7 @@ void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing&
 template <typename T>
 hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, const moe_routing& r,
                  const void* y_sorted, const void* saved, const void* grad_out, void* grad_x,
-                 const moe_grads& g, void* ws, hipStream_t s) {
+                 const moe_grads& g, void* ws, hipStream_t s, hipStream_t side) {
   const int64_t T_ = p.tokens, S = T_ * p.top_k;
   const int E = p.experts, k = p.top_k, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + E;
@@ -720,13 +720,15 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     }
   };
   if (hs > 0) {
-    SideFork fork;
-    hipError_t e = fork.fork(s);
+    // The shared expert's backward needs only grad_out, x and its saved
+    // activations: with a second stream it runs there beside the routed part.
+    StreamFork fork(s, side);
+    hipError_t e = fork.fork();
     if (e != hipSuccess) return e;
     shared_bwd(fork.side());
     routed_bwd(s);
     e = hipGetLastError();
-    if (e == hipSuccess) e = fork.join(s);
+    if (e == hipSuccess) e = fork.join();
     if (e != hipSuccess) return e;
   } else {
     routed_bwd(s);
@@ -761,7 +763,7 @@ size_t bwd_ws_bytes(const moe_problem& p) { return bwd_layout(p).total; }
 hipError_t launch_bwd(const moe_problem& p, const void* x, const moe_weights& w,
                       const moe_routing& r, const void* y_sorted, const void* saved,
                       const void* grad_out, void* grad_x, const moe_grads& g, void* ws,
-                      hipStream_t s) {
+                      hipStream_t s, hipStream_t side) {
   if (p.tokens == 0) {
     const int64_t E = p.experts, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
     zero(g.w_router, d * E, s);
@@ -776,8 +778,8 @@ hipError_t launch_bwd(const moe_problem& p, const void* x, const moe_weights& w,
     return hipGetLastError();
   }
   if (p.dtype == MOE_BF16)
-    return bwd_t<bf16_t>(p, x, w, r, y_sorted, saved, grad_out, grad_x, g, ws, s);
-  return bwd_t<float>(p, x, w, r, y_sorted, saved, grad_out, grad_x, g, ws, s);
+    return bwd_t<bf16_t>(p, x, w, r, y_sorted, saved, grad_out, grad_x, g, ws, s, side);
+  return bwd_t<float>(p, x, w, r, y_sorted, saved, grad_out, grad_x, g, ws, s, side);
 }
 
 }  // namespace moe

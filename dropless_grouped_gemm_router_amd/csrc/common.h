@@ -108,32 +108,33 @@ int persistent_slots(const void* kernel, int threads);
 // Compute units of the current device.
 int cu_count();
 
-// Fork onto and join back from the current device's side stream (default
-// priority, non-blocking; created on first use and kept for the process).
-// The object holds a process-wide lock from construction to destruction, so
-// concurrent callers never interleave records and waits on the shared fork,
-// mark and join events; work enqueued on side() between fork(s) and join(s) runs
-// beside s, after everything enqueued on s before the fork, and s waits for
-// it from the join on.
-// Runs a call's independent part on the device's side stream. While the
-// kernel timer is on, the "side stream" is the caller's stream itself, so
-// each timed kernel runs alone and its events bracket its own duration.
-class SideFork {
+// Runs a call's independent part on a second stream that the caller
+// passes (side may be null: no second stream, everything on s). The fork,
+// mark and join events are created by fork() and released by the
+// destructor, so the library itself keeps no stream or event between calls.
+// Work enqueued on side() between fork() and join() runs beside s, after
+// everything enqueued on s before the fork, and s waits for it from the
+// join on. mark() records a point on the side stream that s waits for at
+// wait_mark(). If a call returns between fork() and join() (an error path),
+// the destructor still joins, so nothing enqueued on the side stream stays
+// unordered against s. While the kernel timer is on, the second stream is s
+// itself, so each timed kernel runs alone.
+class StreamFork {
  public:
-  SideFork();
-  hipError_t fork(hipStream_t s);
-  // A point on the side stream (mark, after the work enqueued there so far)
-  // that s waits for (wait_mark) before the work enqueued on it next.
+  StreamFork(hipStream_t s, hipStream_t side);
+  ~StreamFork();
+  StreamFork(const StreamFork&) = delete;
+  StreamFork& operator=(const StreamFork&) = delete;
+  hipError_t fork();
   hipError_t mark();
-  hipError_t wait_mark(hipStream_t s);
-  hipError_t join(hipStream_t s);
-  hipStream_t side() const { return side_; }
+  hipError_t wait_mark();
+  hipError_t join();
+  hipStream_t side() const { return forked_ ? side_ : caller_; }
 
  private:
-  std::lock_guard<std::mutex> lock_;
-  int dev_ = 0;
-  hipStream_t side_ = nullptr;
-  hipStream_t caller_ = nullptr;
+  hipStream_t caller_, side_;
+  bool forked_ = false, joined_ = false;
+  hipEvent_t ev_fork_ = nullptr, ev_mark_ = nullptr, ev_join_ = nullptr;
 };
 
 // Per-kernel event timing (trace.cpp); no-ops unless moe_trace_enable(1).
@@ -210,12 +211,12 @@ struct ForwardLayout {
 ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training);
 hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* saved, void* out, void* ws,
-                          hipStream_t s);
+                          hipStream_t s, hipStream_t side);
 
 size_t bwd_ws_bytes(const moe_problem& p);
 hipError_t launch_bwd(const moe_problem& p, const void* x, const moe_weights& w,
                       const moe_routing& r, const void* y_sorted, const void* saved,
                       const void* grad_out, void* grad_x, const moe_grads& g, void* ws,
-                      hipStream_t s);
+                      hipStream_t s, hipStream_t side);
 
 }  // namespace moe

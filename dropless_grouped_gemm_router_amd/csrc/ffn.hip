@@ -347,13 +347,12 @@ ForwardLayout forward_layout(const moe_problem& p, int dispatch, bool training) 
 
 namespace {
 
-// route -> permute -> routed FFN on s.
 // route -> permute -> routed FFN on s. With a fork, the routed weights were
 // packed on its side stream before its mark, which s waits for first.
 hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* saved, void* ws,
                           void* x_sorted, void* permute_ws, hipStream_t s,
-                          SideFork* fork = nullptr) {
+                          StreamFork* fork = nullptr) {
   hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
                               r.topk_idx, r.topk_w, s);
   if (e != hipSuccess) return e;
@@ -361,7 +360,7 @@ hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights
                      r.expert_offsets, r.perm, r.inv_perm, r.tiles, r.num_tiles, permute_ws, s);
   if (e != hipSuccess) return e;
   if (fork) {
-    e = fork->wait_mark(s);
+    e = fork->wait_mark();
     if (e != hipSuccess) return e;
   }
   const bool packed = fork != nullptr;
@@ -374,21 +373,21 @@ hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights
 
 hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* saved, void* out, void* ws,
-                          hipStream_t s) {
+                          hipStream_t s, hipStream_t side) {
   const ForwardLayout L = forward_layout(p, dispatch, saved != nullptr);
   char* W = static_cast<char*>(ws);
   void* shared_out = p.d_shared > 0 && !L.fused ? W + L.shared_out : nullptr;
   void* x_sorted = dispatch == MOE_DISPATCH_SORTED ? W + L.x_sorted : nullptr;
   const bool bf = p.dtype == MOE_BF16;
   // Unfused, the shared expert depends on nothing but the tokens and its
-  // weights: it runs on the side stream beside route, permute and the routed
-  // FFN, and the combine waits for it.
-  if (p.d_shared > 0 && !L.fused) {
+  // weights: with a second stream it runs there beside route, permute and
+  // the routed FFN, and the combine waits for it.
+  if (p.d_shared > 0 && !L.fused && side != nullptr && side != s) {
     // The routed weights are packed first on the side stream too, beside the
     // router kernel (which leaves room on every CU for the pack kernel's
     // workgroups); the routed GEMMs wait for that mark.
-    SideFork fork;
-    hipError_t e = fork.fork(s);
+    StreamFork fork(s, side);
+    hipError_t e = fork.fork();
     if (e != hipSuccess) return e;
     if (bf) pack_routed_t<bf16_t>(p, w, ws, saved != nullptr, fork.side());
     else pack_routed_t<float>(p, w, ws, saved != nullptr, fork.side());
@@ -398,7 +397,7 @@ hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, con
     else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
     e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s, &fork);
     if (e == hipSuccess) e = hipGetLastError();
-    if (e == hipSuccess) e = fork.join(s);
+    if (e == hipSuccess) e = fork.join();
     if (e != hipSuccess) return e;
     return launch_combine(p.dtype, p.tokens, p.top_k, p.d_model, y_sorted, r.topk_w, r.inv_perm,
                           shared_out, out, s);

@@ -1,5 +1,5 @@
-// Resident-workgroup counts for persistent kernels, and the side stream that
-// runs the shared expert beside the routed path.
+// Resident-workgroup counts for persistent kernels, and the fork/join of a
+// call's shared-expert work onto the caller's second stream.
 #include <hip/hip_runtime.h>
 
 #include <map>
@@ -47,56 +47,44 @@ int cu_count() {
   return cus;
 }
 
-namespace {
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-hipStream_t g_side[kMaxDevices];
-hipEvent_t g_fork[kMaxDevices], g_join[kMaxDevices], g_mark[kMaxDevices];
-}  // namespace
+StreamFork::StreamFork(hipStream_t s, hipStream_t side) : caller_(s), side_(side) {}
 
-SideFork::SideFork() : lock_(g_side_mu) {}
-
-hipError_t SideFork::fork(hipStream_t s) {
-  caller_ = s;
-  if (trace_on()) {
-    side_ = s;
-    return hipSuccess;
-  }
-  hipError_t e = hipGetDevice(&dev_);
-  if (e == hipSuccess && (dev_ < 0 || dev_ >= kMaxDevices)) e = hipErrorInvalidDevice;
-  if (e != hipSuccess) return e;
-  if (!g_side[dev_]) {
-    e = hipStreamCreateWithFlags(&g_side[dev_], hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_fork[dev_], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_join[dev_], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&g_mark[dev_], hipEventDisableTiming);
-    if (e != hipSuccess) {
-      g_side[dev_] = nullptr;
-      return e;
-    }
-  }
-  e = hipEventRecord(g_fork[dev_], s);
-  if (e == hipSuccess) e = hipStreamWaitEvent(g_side[dev_], g_fork[dev_], 0);
-  if (e == hipSuccess) side_ = g_side[dev_];
+hipError_t StreamFork::fork() {
+  if (side_ == nullptr || side_ == caller_ || trace_on()) return hipSuccess;
+  hipError_t e = hipEventCreateWithFlags(&ev_fork_, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_mark_, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&ev_join_, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(ev_fork_, caller_);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side_, ev_fork_, 0);
+  if (e == hipSuccess) forked_ = true;
   return e;
 }
 
-hipError_t SideFork::mark() {
-  // Nothing to order when the side stream is the caller's own (timer on).
-  if (side_ == nullptr || side_ == caller_) return hipSuccess;
-  return hipEventRecord(g_mark[dev_], side_);
+hipError_t StreamFork::mark() {
+  if (!forked_) return hipSuccess;
+  return hipEventRecord(ev_mark_, side_);
 }
 
-hipError_t SideFork::wait_mark(hipStream_t s) {
-  if (side_ == nullptr || side_ == caller_ || side_ == s) return hipSuccess;
-  return hipStreamWaitEvent(s, g_mark[dev_], 0);
+hipError_t StreamFork::wait_mark() {
+  if (!forked_) return hipSuccess;
+  return hipStreamWaitEvent(caller_, ev_mark_, 0);
 }
 
-hipError_t SideFork::join(hipStream_t s) {
-  if (side_ == s) return hipSuccess;
-  hipError_t e = hipEventRecord(g_join[dev_], side_);
-  if (e == hipSuccess) e = hipStreamWaitEvent(s, g_join[dev_], 0);
+hipError_t StreamFork::join() {
+  if (!forked_ || joined_) return hipSuccess;
+  hipError_t e = hipEventRecord(ev_join_, side_);
+  if (e == hipSuccess) e = hipStreamWaitEvent(caller_, ev_join_, 0);
+  if (e == hipSuccess) joined_ = true;
   return e;
+}
+
+StreamFork::~StreamFork() {
+  (void)join();
+  // An event may be released while work that records or waits for it is
+  // still queued; the runtime frees it once that work has run.
+  if (ev_fork_) (void)hipEventDestroy(ev_fork_);
+  if (ev_mark_) (void)hipEventDestroy(ev_mark_);
+  if (ev_join_) (void)hipEventDestroy(ev_join_);
 }
 
 }  // namespace moe

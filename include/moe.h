@@ -35,16 +35,21 @@
  *   - Values inside device buffers are not checked: an out-of-range expert
  *     index passed to moe_permute, or a routing state not produced by
  *     moe_route/moe_permute for the same problem, is undefined behaviour.
- *   - No global mutable state besides the optional kernel timer below
- *     and, per device, one side stream with three events (all guarded by a
- *     lock): calls on distinct streams may run concurrently from several
- *     host threads. moe_forward and moe_bwd, when the problem has a shared
- *     expert, run the shared expert's kernels on that side stream (default
- *     priority, created on the device's first such call and kept for the
- *     process), forked from and joined back to `stream` with events, so the
- *     caller sees one stream's ordering; moe_forward also packs the routed
- *     experts' weights there first, and its routed GEMMs wait for that. No
- *     device memory is allocated.
+ *   - No global mutable state besides the optional kernel timer below (a
+ *     diagnostic, off unless enabled) and the device address of
+ *     moe_permute_static's fixed scratch, looked up once per device: calls
+ *     on distinct streams may run concurrently from several host threads.
+ *     No device memory is allocated.
+ *   - moe_forward and moe_bwd take an optional second stream, side_stream
+ *     (NULL or equal to `stream`: everything runs on `stream`). With one,
+ *     a problem with a shared expert runs the shared expert's kernels
+ *     there, forked from and joined back to `stream` with events created
+ *     for the call and released with it, so the caller sees one stream's
+ *     ordering and both streams' work is done once `stream` reaches the
+ *     call's end; moe_forward also packs the routed experts' weights there
+ *     first, and its routed GEMMs wait for that. The caller owns the side
+ *     stream; work it already holds runs before the fork point. The results
+ *     are the same bits with or without it.
  *   - Results are deterministic: no floating-point atomics are used, and
  *     repeated calls on the same inputs give identical bits.
  */
@@ -302,7 +307,7 @@ size_t moe_forward_workspace_bytes(const moe_problem* p, int dispatch, int train
  */
 int moe_forward(const moe_problem* p, int dispatch, const void* x, const moe_weights* w,
                 moe_routing* r, void* y_sorted, void* saved, void* out, void* workspace,
-                size_t workspace_bytes, void* stream);
+                size_t workspace_bytes, void* stream, void* side_stream);
 
 /*
  * Train-step backward (gpu_moe_h100.json header: value and gradient with
@@ -322,16 +327,17 @@ int moe_forward(const moe_problem* p, int dispatch, const void* x, const moe_wei
  */
 int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w, const moe_routing* r,
             const void* y_sorted, const void* saved, const void* grad_out, void* grad_x,
-            const moe_grads* g, void* workspace, size_t workspace_bytes, void* stream);
+            const moe_grads* g, void* workspace, size_t workspace_bytes, void* stream,
+            void* side_stream);
 
 /*
  * Kernel timer (host). moe_trace_enable(1) clears the record and starts
  * bracketing every libmoe kernel launch with two hipEvents on its stream;
  * moe_trace_enable(0) stops and clears. Timing adds no device work besides
- * the event records. While it is on, moe_forward and moe_bwd run their
- * shared-expert part on the caller's stream instead of the side stream (the
- * same kernels, in issue order), so every recorded duration is that of a
- * kernel running alone. Returns MOE_OK.
+ * the event records. While it is on, moe_forward and moe_bwd ignore
+ * side_stream and run everything on `stream` (the same kernels, in issue
+ * order), so every recorded duration is that of a kernel running alone.
+ * Returns MOE_OK.
  */
 int moe_trace_enable(int on);
 

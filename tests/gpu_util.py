@@ -52,6 +52,8 @@ class Case:
         self.dev = B.device_inputs(self.inputs)
         self.buf = B.allocate(p, training=training)
         self.training = training
+        # the caller-owned second stream moe_forward and moe_bwd may fork onto
+        self.side = torch.cuda.Stream()
         torch.cuda.synchronize()
 
     def weights(self):

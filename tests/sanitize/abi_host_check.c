@@ -102,23 +102,24 @@ int main(void) {
   CHECK(moe_combine(&p, NULL, &r, NULL, FAKE(0x63000000), NULL) == MOE_ERR_INVALID);
   CHECK(moe_combine(&p, FAKE(0x60000000), &r, FAKE(0x61000004), FAKE(0x63000000), NULL) ==
         MOE_ERR_INVALID);
-  CHECK(moe_forward(&p, 9, x, &w, &r, FAKE(0x60000000), NULL, FAKE(0x63000000), ws, need, NULL) ==
+  CHECK(moe_forward(&p, 9, x, &w, &r, FAKE(0x60000000), NULL, FAKE(0x63000000), ws, need, NULL,
+                    NULL) ==
         MOE_ERR_INVALID);
   CHECK(moe_forward(&p, MOE_DISPATCH_GATHER, x, &w, &r, FAKE(0x60000000), NULL, FAKE(0x63000000),
-                    ws, 16, NULL) == MOE_ERR_WORKSPACE);
+                    ws, 16, NULL, NULL) == MOE_ERR_WORKSPACE);
   moe_weights w_noshared = w;
   w_noshared.ws_up = NULL;
   CHECK(moe_forward(&p, MOE_DISPATCH_FUSED_GSUM, x, &w_noshared, &r, FAKE(0x60000000), NULL,
-                    FAKE(0x63000000), ws, need, NULL) == MOE_ERR_INVALID);
+                    FAKE(0x63000000), ws, need, NULL, NULL) == MOE_ERR_INVALID);
   moe_problem p_h = prob(100, 8, 2, 256, 192, 0, MOE_BF16, 64, 0);
   CHECK(moe_bwd(&p_h, x, &w, &r, FAKE(0x60000000), FAKE(0x70000000), FAKE(0x71000000),
-                FAKE(0x72000000), &g, ws, need, NULL) == MOE_ERR_UNSUPPORTED);
+                FAKE(0x72000000), &g, ws, need, NULL, NULL) == MOE_ERR_UNSUPPORTED);
   CHECK(moe_bwd(&p, x, &w, &r, FAKE(0x60000000), FAKE(0x70000000), FAKE(0x71000000),
-                FAKE(0x72000000), NULL, ws, need, NULL) == MOE_ERR_INVALID);
+                FAKE(0x72000000), NULL, ws, need, NULL, NULL) == MOE_ERR_INVALID);
   CHECK(moe_bwd(&p, x, &w, &r, FAKE(0x60000000), FAKE(0x70000010), FAKE(0x71000000),
-                FAKE(0x72000000), &g, ws, need, NULL) == MOE_ERR_INVALID);
+                FAKE(0x72000000), &g, ws, need, NULL, NULL) == MOE_ERR_INVALID);
   CHECK(moe_bwd(&p, x, &w, &r, FAKE(0x60000000), FAKE(0x70000000), FAKE(0x71000000),
-                FAKE(0x72000000), &g, ws, 16, NULL) == MOE_ERR_WORKSPACE);
+                FAKE(0x72000000), &g, ws, 16, NULL, NULL) == MOE_ERR_WORKSPACE);
   /* zero tokens: successful no-ops that never touch their pointers */
   moe_problem z = prob(0, 8, 2, 256, 128, 0, MOE_BF16, 64, 0);
   CHECK(moe_route(&z, NULL, NULL, NULL, NULL) == MOE_OK);
@@ -126,7 +127,7 @@ int main(void) {
   CHECK(moe_permute_static(&z, NULL, NULL) == MOE_OK);
   CHECK(moe_ffn_fwd(&z, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == MOE_OK);
   CHECK(moe_combine(&z, NULL, NULL, NULL, NULL, NULL) == MOE_OK);
-  CHECK(moe_forward(&z, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == MOE_OK);
+  CHECK(moe_forward(&z, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL, NULL) == MOE_OK);
   char buf[8];
   CHECK(moe_trace_summary(NULL, 0) == MOE_ERR_INVALID);
   CHECK(moe_trace_summary(buf, 1) == MOE_ERR_INVALID || moe_trace_summary(buf, 1) == MOE_OK);

@@ -14,10 +14,13 @@ pytestmark = pytest.mark.gpu
 GRAD_NAMES = ["w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down"]
 
 
-def run_bwd(c: Case):
+def run_bwd(c: Case, side=True):
+    """Staged forward with saved activations, then moe_bwd, by default with
+    a second stream for the shared expert's backward."""
     import torch
     c.forward()
-    gx, g = B.backward(c.p, c.dev["x"], c.weights(), c.dev["grad_out"], c.buf)
+    gx, g = B.backward(c.p, c.dev["x"], c.weights(), c.dev["grad_out"], c.buf,
+                       side_stream=c.side if side else None)
     torch.cuda.synchronize()
     return gx, g
 
@@ -93,6 +96,20 @@ def test_backward_deterministic():
     a = {n: t.clone() for n, t in g.items()}
     ax = gx.clone()
     gx2, g2 = run_bwd(c)
+    assert bool((ax == gx2).all())
+    for n in a:
+        assert bool((a[n] == g2[n]).all()), n
+
+
+def test_backward_side_stream_same_bits():
+    """moe_bwd with and without a second stream: the same kernels in another
+    order across two streams, so identical gradients bit for bit."""
+    p = Problem(1500, 16, 4, 256, 128, 256, "bf16", 128)
+    c = Case(p, seed=6, training=True)
+    gx, g = run_bwd(c, side=True)
+    a = {n: t.clone() for n, t in g.items()}
+    ax = gx.clone()
+    gx2, g2 = run_bwd(c, side=False)
     assert bool((ax == gx2).all())
     for n in a:
         assert bool((a[n] == g2[n]).all()), n

@@ -50,7 +50,8 @@ def bits_equal(a, b) -> bool:
 def run_variant(c: Case, dispatch, training=False):
     import torch
     buf = B.allocate(c.p, training=training, dispatch=dispatch)
-    B.forward_dispatch(c.p, dispatch, c.dev["x"], c.weights(), buf, training=training)
+    B.forward_dispatch(c.p, dispatch, c.dev["x"], c.weights(), buf, training=training,
+                       side_stream=c.side)
     torch.cuda.synchronize()
     return buf
 

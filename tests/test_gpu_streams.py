@@ -1,8 +1,9 @@
 """Streams and graphs around the C ABI (GPU): moe_forward and moe_bwd fork the
-shared expert onto a per-device side stream and join it back, under a lock.
-Concurrent callers on their own streams must get the same bits as a lone
-call, and the whole train step must replay from a captured HIP graph with
-the results of eager calls, replay after replay."""
+shared expert onto the caller's second stream and join it back with events
+made for the call. Concurrent callers, each with its own pair of streams,
+must get the same bits as a lone call, and the whole train step must replay
+from a captured HIP graph with the results of eager calls, replay after
+replay."""
 
 import threading
 
@@ -37,6 +38,7 @@ def test_concurrent_host_threads_match_lone_calls():
         refs.append(buf.out.clone())
     bufs = [B.allocate(c.p, dispatch="gather") for c in cases]
     streams = [torch.cuda.Stream() for _ in cases]
+    sides = [torch.cuda.Stream() for _ in cases]
     errors = []
 
     def run(i):
@@ -44,7 +46,7 @@ def test_concurrent_host_threads_match_lone_calls():
             with torch.cuda.stream(streams[i]):
                 for _ in range(6):
                     B.forward_dispatch(cases[i].p, "gather", cases[i].dev["x"], cases[i].weights(),
-                                       bufs[i])
+                                       bufs[i], side_stream=sides[i])
             streams[i].synchronize()
         except Exception as e:  # noqa: BLE001 - reported below
             errors.append(e)
@@ -61,7 +63,7 @@ def test_concurrent_host_threads_match_lone_calls():
 
 
 def test_back_to_back_forwards_use_their_own_weights():
-    """moe_forward packs the routed weights into the workspace on the side
+    """moe_forward packs the routed weights into the workspace on the second
     stream, and the routed GEMMs wait for that. Calls in a row on one stream
     and one workspace, alternating two weight sets with no synchronisation
     in between, must each give the bits of a lone call with their weights:
@@ -78,10 +80,11 @@ def test_back_to_back_forwards_use_their_own_weights():
         refs.append(buf.out.clone())
     assert not bits_equal(refs[0], refs[1])
     buf = B.allocate(p, dispatch="gather")
+    side = torch.cuda.Stream()
     outs = []
     for i in range(6):
         c = cases[i % 2]
-        B.forward_dispatch(p, "gather", c.dev["x"], c.weights(), buf)
+        B.forward_dispatch(p, "gather", c.dev["x"], c.weights(), buf, side_stream=side)
         outs.append(buf.out.clone())  # the current stream, after the call
     torch.cuda.synchronize()
     for i, o in enumerate(outs):
@@ -98,16 +101,16 @@ def test_train_step_replays_from_a_hip_graph():
     x_buf = c.dev["x"].clone()
     g_buf = c.dev["grad_out"].clone()
     buf = B.allocate(p, training=True, dispatch="gather")
+    side = torch.cuda.Stream()
 
     def step():
-        B.forward_dispatch(p, "gather", x_buf, w, buf, training=True)
-        B.backward(p, x_buf, w, g_buf, buf)
+        B.forward_dispatch(p, "gather", x_buf, w, buf, training=True, side_stream=side)
+        B.backward(p, x_buf, w, g_buf, buf, side_stream=side)
 
     def snapshot():
         return [buf.out.clone(), buf.grad_x.clone()] + [t.clone() for t in buf.grads.values()]
 
-    # Warm up on a side stream (creates the side stream and events before
-    # capture), then capture.
+    # Warm up on a stream of its own, then capture.
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -136,10 +139,11 @@ def test_train_step_replays_from_a_hip_graph():
 
 
 def test_kernel_timer_mode_gives_the_same_bits():
-    """With libmoe's kernel timer on, moe_forward and moe_bwd run the shared
-    expert's part on the caller's stream (so every recorded duration is a
-    kernel's own): the same kernels in issue order, so the same bits as the
-    two-stream call, and every kernel of the step is recorded."""
+    """With libmoe's kernel timer on, moe_forward and moe_bwd ignore the
+    second stream and run the shared expert's part on the caller's stream
+    (so every recorded duration is a kernel's own): the same kernels in
+    issue order, so the same bits as the two-stream call, and every kernel
+    of the step is recorded."""
     import torch
     p = Problem(1500, 8, 2, 256, 128, 128, "bf16", 128)
     c = Case(p, seed=37, training=True)
@@ -147,8 +151,8 @@ def test_kernel_timer_mode_gives_the_same_bits():
     buf = B.allocate(p, training=True, dispatch="gather")
 
     def step():
-        B.forward_dispatch(p, "gather", c.dev["x"], w, buf, training=True)
-        B.backward(p, c.dev["x"], w, c.dev["grad_out"], buf)
+        B.forward_dispatch(p, "gather", c.dev["x"], w, buf, training=True, side_stream=c.side)
+        B.backward(p, c.dev["x"], w, c.dev["grad_out"], buf, side_stream=c.side)
         torch.cuda.synchronize()
         return [buf.out.clone(), buf.grad_x.clone()] + [t.clone() for t in buf.grads.values()]
 
