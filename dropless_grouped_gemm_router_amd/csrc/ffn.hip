@@ -106,6 +106,72 @@ __global__ __launch_bounds__(256) void pack_bf16_kernel(const bf16_t* __restrict
   }
 }
 
+// Several bf16 packs in one launch (the routed gate|up and down weights and
+// the shared expert's, 27 MiB at the measured shape, were four launches of a
+// few microseconds each). Job j packs `groups` matrices as pack_bf16_kernel
+// does; the flat wave-tile index runs over the jobs in order.
+struct PackJob {
+  const bf16_t* s0;
+  const bf16_t* s1;
+  bf16_t* dst;
+  int K, nsrc, interleave, groups;
+};
+constexpr int kMaxPackJobs = 4;
+struct PackJobs {
+  PackJob job[kMaxPackJobs];
+  int end[kMaxPackJobs];  // exclusive end of each job's wave tiles
+  int n;
+};
+
+__global__ __launch_bounds__(256) void pack_bf16_jobs_kernel(const PackJobs jobs) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  int j = 0;
+  while (j < jobs.n && t >= jobs.end[j]) ++j;
+  if (j >= jobs.n) return;
+  const PackJob& b = jobs.job[j];
+  const int local = t - (j ? jobs.end[j - 1] : 0);
+  const int ndst = b.interleave ? 2 * b.nsrc : b.nsrc;
+  const int tiles_p = ndst / kPackTile;
+  const int per_group = tiles_p * (b.K / kPackTile);
+  const int grp = local / per_group, tile = local % per_group;
+  const int lane = threadIdx.x & 63, kb = lane >> 3, pb = lane & 7;
+  const int pr = (tile % tiles_p) * kPackTile + 8 * pb;
+  const int k0 = (tile / tiles_p) * kPackTile + 8 * kb;
+  const int64_t gs = static_cast<int64_t>(b.K) * b.nsrc;
+  const bf16_t* src = b.s0 + grp * gs;
+  int col = pr;
+  if (b.interleave) {
+    col = 16 * (pr / 32) + pr % 16;
+    if (pr % 32 >= 16) src = b.s1 + grp * gs;
+  }
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(k0 + i) * b.nsrc + col);
+  bf16_t* d = b.dst + grp * static_cast<int64_t>(ndst) * b.K;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    u32x4 o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[m] = __builtin_amdgcn_perm(v[2 * m + 1][jj / 2], v[2 * m][jj / 2],
+                                   (jj & 1) ? 0x07060302u : 0x05040100u);
+    *reinterpret_cast<u32x4*>(d + static_cast<int64_t>(pr + jj) * b.K + k0) = o;
+  }
+}
+
+void pack_bf16_jobs(PackJobs& jobs, hipStream_t s) {
+  int total = 0;
+  for (int j = 0; j < jobs.n; ++j) {
+    const PackJob& b = jobs.job[j];
+    const int ndst = b.interleave ? 2 * b.nsrc : b.nsrc;
+    total += (ndst / kPackTile) * (b.K / kPackTile) * b.groups;
+    jobs.end[j] = total;
+  }
+  if (total == 0) return;
+  MOE_LAUNCH("pack_weights", pack_bf16_jobs_kernel, dim3((total + 3) / 4), dim3(256), 0, s, jobs);
+}
+
 template <typename T>
 void pack(const void* s0, const void* s1, void* dst, int groups, int K, int nsrc, bool il,
           hipStream_t s) {
@@ -236,16 +302,37 @@ void shared_ffn(const moe_problem& p, const void* x, const void* sgu, const void
   }
 }
 
-// The routed experts' weights in the GEMMs' layout (workspace). Depends on
-// the weights alone, so it may run on another stream before the routing.
+// The routed experts' weights (and, with `shared`, the shared expert's) in
+// the GEMMs' layout (workspace). Depends on the weights alone, so it may run
+// on another stream before the routing. bf16: one launch for all of them.
 template <typename T>
-void pack_routed_t(const moe_problem& p, const moe_weights& w, void* ws, bool training,
-                   hipStream_t s) {
+void pack_weights_t(const moe_problem& p, const moe_weights& w, void* ws, bool training,
+                    bool shared, hipStream_t s) {
   const FfnLayout L = ffn_layout(p, training);
   char* W = static_cast<char*>(ws);
-  const int E = p.experts, d = p.d_model, h = p.d_hidden;
+  const int E = p.experts, d = p.d_model, h = p.d_hidden, hs = p.d_shared;
+  shared = shared && hs > 0;
+  if (std::is_same<T, bf16_t>::value) {
+    PackJobs jobs{};
+    auto add = [&](const void* a, const void* b, char* dst, int groups, int K, int nsrc, bool il) {
+      jobs.job[jobs.n++] = PackJob{static_cast<const bf16_t*>(a), static_cast<const bf16_t*>(b),
+                                   reinterpret_cast<bf16_t*>(dst), K, nsrc, il ? 1 : 0, groups};
+    };
+    add(w.w_gate, w.w_up, W + L.gu_packed, E, d, h, true);
+    add(w.w_down, nullptr, W + L.down_packed, E, h, d, false);
+    if (shared) {
+      add(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true);
+      add(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false);
+    }
+    pack_bf16_jobs(jobs, s);
+    return;
+  }
   pack<T>(w.w_gate, w.w_up, W + L.gu_packed, E, d, h, true, s);
   pack<T>(w.w_down, nullptr, W + L.down_packed, E, h, d, false, s);
+  if (shared) {
+    pack<T>(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true, s);
+    pack<T>(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false, s);
+  }
 }
 
 // Routed part: pack the expert weights (unless `packed`: already enqueued,
@@ -259,7 +346,7 @@ void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
   char* W = static_cast<char*>(ws);
   char* SV = static_cast<char*>(saved);
   const int h = p.d_hidden;
-  if (!packed) pack_routed_t<T>(p, w, ws, saved != nullptr, s);
+  if (!packed) pack_weights_t<T>(p, w, ws, saved != nullptr, false, s);
   T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
@@ -272,13 +359,16 @@ void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
 // routed part on another stream.
 template <typename T>
 void ffn_shared_t(const moe_problem& p, const void* x, const moe_weights& w, void* shared_out,
-                  void* saved, void* ws, const FuseCombine* fuse, hipStream_t s) {
+                  void* saved, void* ws, const FuseCombine* fuse, hipStream_t s,
+                  bool packed = false) {
   const FfnLayout L = ffn_layout(p, saved != nullptr);
   char* W = static_cast<char*>(ws);
   char* SV = static_cast<char*>(saved);
   const int d = p.d_model, hs = p.d_shared;
-  pack<T>(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true, s);
-  pack<T>(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false, s);
+  if (!packed) {
+    pack<T>(w.ws_gate, w.ws_up, W + L.sgu_packed, 1, d, hs, true, s);
+    pack<T>(w.ws_down, nullptr, W + L.sdown_packed, 1, hs, d, false, s);
+  }
   T* hsb = saved ? reinterpret_cast<T*>(SV + L.sv_sh) : reinterpret_cast<T*>(W + L.h_shared);
   T* ssa = saved ? reinterpret_cast<T*>(SV + L.sv_sab) : nullptr;
   T* ssb = saved ? ssa + hs : nullptr;
@@ -289,8 +379,9 @@ template <typename T>
 hipError_t ffn_fwd_t(const moe_problem& p, const void* x, const moe_weights& w,
                      const moe_routing& r, void* y_sorted, void* shared_out, void* saved,
                      void* ws, void* x_sorted, const FuseCombine* fuse, hipStream_t s) {
-  ffn_routed_t<T>(p, x, w, r, y_sorted, saved, ws, x_sorted, s);
-  if (p.d_shared > 0) ffn_shared_t<T>(p, x, w, shared_out, saved, ws, fuse, s);
+  pack_weights_t<T>(p, w, ws, saved != nullptr, true, s);
+  ffn_routed_t<T>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, true);
+  if (p.d_shared > 0) ffn_shared_t<T>(p, x, w, shared_out, saved, ws, fuse, s, true);
   return hipGetLastError();
 }
 
@@ -352,7 +443,7 @@ namespace {
 hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights& w,
                           const moe_routing& r, void* y_sorted, void* saved, void* ws,
                           void* x_sorted, void* permute_ws, hipStream_t s,
-                          StreamFork* fork = nullptr) {
+                          StreamFork* fork = nullptr, bool packed = false) {
   hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
                               r.topk_idx, r.topk_w, s);
   if (e != hipSuccess) return e;
@@ -363,7 +454,7 @@ hipError_t routed_forward(const moe_problem& p, const void* x, const moe_weights
     e = fork->wait_mark();
     if (e != hipSuccess) return e;
   }
-  const bool packed = fork != nullptr;
+  packed = packed || fork != nullptr;
   if (p.dtype == MOE_BF16) ffn_routed_t<bf16_t>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, packed);
   else ffn_routed_t<float>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, packed);
   return hipGetLastError();
@@ -389,12 +480,12 @@ hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, con
     StreamFork fork(s, side);
     hipError_t e = fork.fork();
     if (e != hipSuccess) return e;
-    if (bf) pack_routed_t<bf16_t>(p, w, ws, saved != nullptr, fork.side());
-    else pack_routed_t<float>(p, w, ws, saved != nullptr, fork.side());
+    if (bf) pack_weights_t<bf16_t>(p, w, ws, saved != nullptr, true, fork.side());
+    else pack_weights_t<float>(p, w, ws, saved != nullptr, true, fork.side());
     e = fork.mark();
     if (e != hipSuccess) return e;
-    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
-    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, nullptr, fork.side());
+    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, nullptr, fork.side(), true);
+    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, nullptr, fork.side(), true);
     e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s, &fork);
     if (e == hipSuccess) e = hipGetLastError();
     if (e == hipSuccess) e = fork.join();
@@ -402,13 +493,17 @@ hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, con
     return launch_combine(p.dtype, p.tokens, p.top_k, p.d_model, y_sorted, r.topk_w, r.inv_perm,
                           shared_out, out, s);
   }
-  hipError_t e = routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s);
+  // One stream: every weight pack first (one launch in bf16), then the path.
+  if (bf) pack_weights_t<bf16_t>(p, w, ws, saved != nullptr, true, s);
+  else pack_weights_t<float>(p, w, ws, saved != nullptr, true, s);
+  hipError_t e =
+      routed_forward(p, x, w, r, y_sorted, saved, ws, x_sorted, W + L.permute, s, nullptr, true);
   if (e != hipSuccess) return e;
   if (p.d_shared > 0) {
     // fused: the shared down GEMM's epilogue reads the routed outputs
     const FuseCombine fuse{out, y_sorted, r.topk_w, r.inv_perm};
-    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, L.fused ? &fuse : nullptr, s);
-    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, L.fused ? &fuse : nullptr, s);
+    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, L.fused ? &fuse : nullptr, s, true);
+    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, L.fused ? &fuse : nullptr, s, true);
   }
   e = hipGetLastError();
   if (e != hipSuccess || L.fused) return e;
