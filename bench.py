@@ -28,8 +28,9 @@ PEAK_HBM_GBS = 8000.0
 PEAK_VALU_TFLOPS = 78.6
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_TRAIN_FILE = os.path.join(ROOT, "profiles", "traffic_train.json")
 KERNEL_SOURCES = ["gemm_core.h", "gemm_wide.h", "gemm_launch.h", "ffn.hip", "route.hip",
-                  "permute.hip", "combine.hip", "common.h", "sort_rows.h"]
+                  "permute.hip", "combine.hip", "common.h", "sort_rows.h", "bwd.hip", "gemm_wgrad.h"]
 
 
 def kernel_source_hash():
@@ -125,27 +126,65 @@ def roofline_of(kname, flops, nbytes, avg_ms, dtype):
 
 
 def trace_name(kernel):
-    """libmoe trace name of a compiled forward kernel, from its signature."""
+    """libmoe trace name of a compiled kernel, from its signature. Kernels
+    that serve two stages of one step get the first stage's name here;
+    ``step_trace_names`` tells the launches apart by their order."""
     import re
     if "route_kernel" in kernel or "route_resident_kernel" in kernel:
         return "route"
+    for k, name in (("combine_bwd", "bwd_combine"), ("router_partial", "bwd_router_partial"),
+                    ("router_reduce", "bwd_router_reduce"), ("router_transpose", "bwd_router_transpose"),
+                    ("split_reduce", "bwd_split_reduce"), ("dx_gather", "bwd_dx"),
+                    ("fill_zero", "fill_zero"), ("retile", "retile")):
+        if f"{k}_kernel" in kernel or f"{k}_k_kernel" in kernel:
+            return name
     if "combine_kernel" in kernel or "combine_k_kernel" in kernel:
         return "combine"
     for k in ("count", "scan", "scatter"):
         if f"{k}_kernel" in kernel:
             return f"permute_{k}"
-    if "pack_kernel" in kernel or "pack_bf16_kernel" in kernel:
+    if "pack_kernel" in kernel or "pack_bf16" in kernel:
         return "pack_weights"
     if "sort_rows_kernel" in kernel:
         return "sort_rows"
+    m = re.search(r"wgrad(?:_tr)?_kernel<.*>, (true|false), (true|false)>", kernel)
+    if m:
+        if m.group(1) == "true":
+            return "bwd_shared_wgrad_down"
+        return "bwd_wgrad_gate_up" if m.group(2) == "true" else "bwd_wgrad_down"
     m = (re.search(r"wide_gemm_kernel<(true|false), (\d), (true|false)>", kernel) or
-         re.search(r"gemm_kernel<[^>]*>, (true|false), (\d), (true|false)>", kernel))
+         re.search(r"gemm_kernel<.*>, (true|false), (\d), (true|false)>", kernel))
     if m:
         gather, epi, dense = m.group(1) == "true", int(m.group(2)), m.group(3) == "true"
+        if epi == 2:
+            return "bwd_shared_down_dgrad" if dense else "bwd_down_dgrad"
         if dense:
             return {1: "shared_gate_up", 3: "shared_down_combine"}.get(epi, "shared_down")
         return "gemm_gate_up" if epi == 1 else "gemm_down"
     return None
+
+
+# A compiled kernel that serves two stages of a train step: its n-th launch
+# within one step is the n-th stage named here.
+_SECOND_USE = {"shared_down": "bwd_shared_gate_up_dgrad", "gemm_down": "bwd_gate_up_dgrad",
+               "bwd_shared_wgrad_down": "bwd_shared_wgrad_gate_up", "retile": "bwd_retile",
+               "bwd_split_reduce": "bwd_split_reduce_gate_up"}
+
+
+def step_trace_names(kernels):
+    """Trace names of a sequence of launches (in dispatch order) made by
+    whole steps, each opening with the weight pack: a kernel's second launch
+    within a step is the second stage it serves (``_SECOND_USE``)."""
+    names, seen = [], set()
+    for k in kernels:
+        n = trace_name(k)
+        if n == "pack_weights":
+            seen = set()
+        if n in seen and n in _SECOND_USE:
+            n = _SECOND_USE[n]
+        seen.add(n)
+        names.append(n)
+    return names
 
 
 def reference_rates(steps, warmup):
@@ -196,38 +235,61 @@ def reference_rates(steps, warmup):
     return lines
 
 
+def load_traffic(path, workload_name):
+    """Per-kernel counter bytes from a committed traffic summary, or {} when
+    it was taken on another workload or before the kernel sources changed."""
+    try:
+        with open(path) as fh:
+            tr = json.load(fh)
+    except (OSError, ValueError):
+        return {}
+    if tr.get("source_hash") != kernel_source_hash() or tr.get("workload") != workload_name:
+        return {}
+    return tr.get("kernels", {})
+
+
 def pmc_summary(fetch_dir, write_dir, copyf_dir, copyw_dir, workload_name, out_path):
-    """HBM bytes per launch of each forward kernel from rocprofv3 FETCH_SIZE
-    and WRITE_SIZE runs (KiB per dispatch), each scaled by what the same
-    counter reports for a plain device copy of known size."""
+    """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
+    reports for a plain device copy of known size. Launches are named in
+    dispatch order (``step_trace_names``); a name's figure is the median over
+    its launches."""
     import csv
     import statistics
 
-    def per_kernel(d, counter):
-        vals = {}
+    def per_dispatch(d, counter):
+        rows = []
         with open(os.path.join(d, "run_counter_collection.csv")) as fh:
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] == counter:
-                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        rows.sort()
+        return rows
+
+    def per_name(d, counter):
+        rows = per_dispatch(d, counter)
+        vals = {}
+        for n, (_, _, v) in zip(step_trace_names([k for _, k, _ in rows]), rows):
+            if n is not None:
+                vals.setdefault(n, []).append(v)
         return vals
 
     def copy_scale(d, counter):
-        vals = per_kernel(d, counter)
-        kib = [v for k, vs in vals.items() if "copyBuffer" in k for v in vs]
+        kib = [v for _, k, v in per_dispatch(d, counter) if "copyBuffer" in k]
         n = 1024 << 20  # the calibration copies 1024 MiB
         return n / (statistics.median(kib) * 1024.0)
 
     fs, ws = copy_scale(copyf_dir, "FETCH_SIZE"), copy_scale(copyw_dir, "WRITE_SIZE")
-    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    fetch, write = per_name(fetch_dir, "FETCH_SIZE"), per_name(write_dir, "WRITE_SIZE")
     out = {"workload": workload_name, "source_hash": kernel_source_hash(),
            "fetch_scale": fs, "write_scale": ws, "kernels": {}}
-    for k, fv in fetch.items():
-        name = trace_name(k)
-        if name is None or k not in write:
+    for name, fv in fetch.items():
+        if name not in write:
             continue
         fb = statistics.median(fv) * 1024.0 * fs
-        wb = statistics.median(write[k]) * 1024.0 * ws
-        out["kernels"][name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+        wb = statistics.median(write[name]) * 1024.0 * ws
+        out["kernels"][name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb,
+                                "launches": len(fv)}
     with open(out_path, "w") as fh:
         json.dump(out, fh, indent=1, sort_keys=True)
     print(json.dumps(out, indent=1, sort_keys=True))
@@ -294,7 +356,7 @@ def pages_timing(step, ms_hint, samples=21):
             "q1_ms": q[0], "q3_ms": q[2], "min_ms": per[0], "max_ms": per[-1]}
 
 
-def train_step_line(B, steps, warmup, tokens=0):
+def train_step_line(B, steps, warmup, tokens=0, pages=True):
     """Forward + backward on the train-step workload (16384 tokens, or
     `tokens` of the same layer)."""
     import dataclasses
@@ -318,7 +380,7 @@ def train_step_line(B, steps, warmup, tokens=0):
         B.backward(p, x, dev, g, buf, side_stream=side)
 
     ms = time_steps(step, steps, warmup)
-    pages = pages_timing(step, ms)
+    pages = pages_timing(step, ms) if pages else None
     # per-kernel times of the same steps, from libmoe's HIP events (with the
     # kernel timer on, the second stream is not used, so each duration is
     # that of the kernel alone)
@@ -332,12 +394,15 @@ def train_step_line(B, steps, warmup, tokens=0):
     wk.update(bwd_work(p))
     avg = {kn: v["ms"] / v["count"] for kn, v in kern.items()}
     roofs = {kn: roofline_of(kn, wk[kn][0], wk[kn][1], avg[kn], p.dtype) for kn in wk if kn in avg}
+    traffic = load_traffic(TRAFFIC_TRAIN_FILE, name)
     return {"workload": name, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
             "pages_timing": pages,
             "tflops_3x_fwd": 3 * fwd / (ms * 1e-3) / 1e12, "steps": steps, "warmup": warmup,
             "kernels_ms_per_step": {kn: round(v["ms"] / steps, 5) for kn, v in sorted(kern.items())},
             "kernel_rooflines": {kn: {"frac": round(r["frac"], 4), "achieved": round(r["achieved"], 1),
-                                      "unit": r["unit"], "bound": r["bound"]}
+                                      "unit": r["unit"], "bound": r["bound"],
+                                      "traffic": (round(traffic[kn]["bytes_per_launch"])
+                                                  if kn in traffic else None)}
                                  for kn, r in sorted(roofs.items())}}
 
 
@@ -431,6 +496,8 @@ def main():
                     help="tokens the CPU oracle runs on (about 10 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--no-pages", action="store_true",
+                    help="skip the pages' sampled timing (short runs under a profiler)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one forward step captured in a HIP graph")
     ap.add_argument("--maxtok", action="store_true",
@@ -444,11 +511,16 @@ def main():
                     help="only time reference rates on this GPU: a plain device copy and the "
                          "vendor BLAS (torch.matmul) on this layer's GEMM shapes")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
-                    help="write profiles/traffic.json from rocprofv3 --pmc output directories")
+                    help="write profiles/traffic.json (with --train-tokens: traffic_train.json) "
+                         "from rocprofv3 --pmc output directories")
     args = ap.parse_args()
     if args.pmc_summary:
         from dropless_grouped_gemm_router_amd.inputs import WORKLOADS
-        pmc_summary(*args.pmc_summary, WORKLOADS[args.workload][0], TRAFFIC_FILE)
+        if args.train_tokens:
+            name = WORKLOADS[4][0].replace("16384 tok", f"{args.train_tokens} tok")
+            pmc_summary(*args.pmc_summary, name, TRAFFIC_TRAIN_FILE)
+        else:
+            pmc_summary(*args.pmc_summary, WORKLOADS[args.workload][0], TRAFFIC_FILE)
         return
     if args.calibrate_copy:
         import torch
@@ -484,7 +556,8 @@ def main():
     if args.train_tokens:
         torch.cuda.set_device(0)
         print(json.dumps({"train_step": train_step_line(B, max(3, min(args.steps, 20)),
-                                                        max(2, args.warmup), args.train_tokens)}),
+                                                        max(2, args.warmup), args.train_tokens,
+                                                        pages=not args.no_pages)}),
               flush=True)
         return
 
@@ -529,8 +602,10 @@ def main():
         torch.cuda.synchronize()
     print(f"bench: warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
     ms = time_steps(timed, args.steps, 0)
-    print("bench: pages' timing protocol", file=sys.stderr, flush=True)
-    pages = pages_timing(timed, ms)
+    pages = None
+    if not args.no_pages:
+        print("bench: pages' timing protocol", file=sys.stderr, flush=True)
+        pages = pages_timing(timed, ms)
     # Per-kernel times: libmoe's HIP events bracket every launch. In the
     # timed steps the shared expert runs beside the routed path on a second
     # stream, so kernel durations there include time shared with other
@@ -549,15 +624,8 @@ def main():
     rooflines = {k: roofline_of(k, wk[k][0], wk[k][1], avg[k], p.dtype) for k in wk if k in avg}
     roof = dict(rooflines[dom]) if dom in rooflines else None
     if roof is not None:
-        roof["traffic"] = None
-        try:
-            with open(TRAFFIC_FILE) as fh:
-                tr = json.load(fh)
-            ent = tr.get("kernels", {}).get(dom)
-            if ent and tr.get("source_hash") == kernel_source_hash() and tr.get("workload") == name:
-                roof["traffic"] = ent["bytes_per_launch"]
-        except (OSError, ValueError):
-            pass
+        ent = load_traffic(TRAFFIC_FILE, name).get(dom)
+        roof["traffic"] = ent["bytes_per_launch"] if ent else None
     peak = PEAK_TFLOPS[p.dtype]
     routed_ms = sum(avg[k] for k in ("gemm_gate_up", "gemm_down") if k in avg)
     routed_fl = wk["gemm_gate_up"][0] + wk["gemm_down"][0]
@@ -581,7 +649,8 @@ def main():
                    "block_m": p.block_m, "skew": p.skew, "dispatch": args.dispatch,
                    "routing": "capacity" if p.capacity else "dropless", "capacity": p.capacity,
                    "hip_graph": bool(args.graph)},
-        "pages_timing": dict(pages, tokens_per_s_median=p.tokens / (pages["median_ms"] * 1e-3)),
+        "pages_timing": (dict(pages, tokens_per_s_median=p.tokens / (pages["median_ms"] * 1e-3))
+                         if pages else None),
         "tflops": total_fl / (ms * 1e-3) / 1e12,
         "grouped_gemm_pct_mfma_peak": 100.0 * routed_fl / (routed_ms * 1e-3) / 1e12 / peak,
         "roofline": roof,
@@ -595,7 +664,7 @@ def main():
     }
     if not args.no_train:
         print("bench: train step", file=sys.stderr, flush=True)
-        line["train_step"] = train_step_line(B, max(5, args.steps // 5), 3)
+        line["train_step"] = train_step_line(B, max(5, args.steps // 5), 3, pages=not args.no_pages)
     if not args.no_cpu_baseline:
         print("bench: CPU oracle baseline", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(p, inputs, min(args.cpu_sample, p.tokens))
