@@ -81,21 +81,33 @@ def bwd_work(p):
     S = T * k
     es = 2 if p.dtype == "bf16" else 4
     w = {
-        # grad_out and y read, dY written, weights / slot map read, dl written
-        "bwd_combine": (2 * S * d, T * d * es + S * d * es + S * d * es + S * 12),
         # token rows and dl read, per-piece partials written
         "bwd_router_partial": (2 * S * d, T * d * es + S * 8 + ((S + p.block_m - 1) // p.block_m + E) * d * 4),
-        # dY, down weights and saved gate/up read, dA|dB written
-        "bwd_down_dgrad": (2 * S * d * h, S * d * es + E * h * d * es + 2 * S * 2 * h * es),
         # dA|dB and gate/up weights read, per-slot dX written
         "bwd_gate_up_dgrad": (2 * S * 2 * h * d, S * 2 * h * es + E * 2 * h * d * es + S * d * es),
-        # H and dY read, fp32 dW_down written
-        "bwd_wgrad_down": (2 * S * h * d, S * h * es + S * d * es + E * h * d * 4),
         # token rows and dA|dB read, fp32 dW_gate, dW_up written
         "bwd_wgrad_gate_up": (2 * S * d * 2 * h, T * d * es + S * 2 * h * es + E * d * 2 * h * 4),
         # per-slot dX, router term and shared dx read, grad_x written
         "bwd_dx": (2 * S * d, S * d * es + E * d * 4 + S * 8 + 2 * T * d * es),
     }
+    if p.dtype == "bf16":
+        w.update({
+            # grad_out rows (once), down weights, saved gate/up and the sorted
+            # rows' combine weights read; dA|dB, w H and the dw parts written
+            "bwd_down_dgrad": (2 * S * d * h, T * d * es + E * h * d * es + S * 2 * h * es + S * 4
+                               + S * 2 * h * es + S * h * es + (h // 128) * S * 4),
+            # grad_out rows (once) and w H read, fp32 dW_down written
+            "bwd_wgrad_down": (2 * S * h * d, T * d * es + S * h * es + E * h * d * 4),
+        })
+    else:
+        w.update({
+            # grad_out and y read, dY written, weights / slot map read, dl written
+            "bwd_combine": (2 * S * d, T * d * es + S * d * es + S * d * es + S * 12),
+            # dY, down weights and saved gate/up read, dA|dB written
+            "bwd_down_dgrad": (2 * S * d * h, S * d * es + E * h * d * es + 2 * S * 2 * h * es),
+            # H and dY read, fp32 dW_down written
+            "bwd_wgrad_down": (2 * S * h * d, S * h * es + S * d * es + E * h * d * 4),
+        })
     if hs:
         w.update({
             "bwd_shared_down_dgrad": (2 * T * d * hs, T * d * es + hs * d * es + 2 * T * 2 * hs * es),
@@ -246,6 +258,41 @@ def load_traffic(path, workload_name):
     if tr.get("source_hash") != kernel_source_hash() or tr.get("workload") != workload_name:
         return {}
     return tr.get("kernels", {})
+
+
+STAGE_PROBE_MODES = {0: "no loads (operands stay in LDS)", 1: "token half loaded (32 KiB)",
+                     2: "weight half loaded (32 KiB)", 3: "whole stage loaded (64 KiB)",
+                     4: "64 KiB into registers", 5: "64 KiB of LDS stores, no loads",
+                     6: "64 KiB issued by waves 0-3 only"}
+
+
+def stage_probe(reps=20):
+    """The wide GEMM engine's K-stage loop on its own (libmoe_probe.so):
+    256 persistent 8-wave workgroups, 16 tiles of 256 x 256 x 512 each, with
+    each stage's loads varied. One JSON line per configuration."""
+    import ctypes
+
+    import torch
+
+    torch.cuda.set_device(0)
+    lib = ctypes.CDLL(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "libmoe_probe.so"))
+    lib.moe_stage_probe.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    grid, items = 256, 16
+    flops = 2.0 * 256 * 256 * 512 * grid * items
+    regions = [(4096, 0, "4 MiB of token rows in order (L2)"),
+               (131072, 1, "rows hashed over 128 MiB (Infinity Cache)"),
+               (1 << 20, 1, "rows hashed over 1 GiB (HBM)")]
+    runs = [(m, regions[0]) for m in range(7)] + [(3, regions[1]), (3, regions[2])]
+    for mode, (rows, rnd, where) in runs:
+        ms = ctypes.c_float(0.0)
+        rc = lib.moe_stage_probe(mode, rows, rnd, grid, items, reps, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"moe_stage_probe(mode {mode}) returned {rc}")
+        tf = flops / (ms.value * 1e-3) / 1e12
+        print(json.dumps({"stage_probe": STAGE_PROBE_MODES[mode], "mode": mode, "tokens": where,
+                          "ms": round(ms.value, 4), "TFLOP/s": round(tf, 1),
+                          "frac_mfma_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}), flush=True)
 
 
 def pmc_summary(fetch_dir, write_dir, copyf_dir, copyw_dir, workload_name, out_path):
@@ -510,6 +557,8 @@ def main():
     ap.add_argument("--reference", action="store_true",
                     help="only time reference rates on this GPU: a plain device copy and the "
                          "vendor BLAS (torch.matmul) on this layer's GEMM shapes")
+    ap.add_argument("--stage-probe", action="store_true",
+                    help="only run the stage-loop probe of the wide GEMM engine (libmoe_probe.so)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
                     help="write profiles/traffic.json (with --train-tokens: traffic_train.json) "
                          "from rocprofv3 --pmc output directories")
@@ -521,6 +570,9 @@ def main():
             pmc_summary(*args.pmc_summary, name, TRAFFIC_TRAIN_FILE)
         else:
             pmc_summary(*args.pmc_summary, WORKLOADS[args.workload][0], TRAFFIC_FILE)
+        return
+    if args.stage_probe:
+        stage_probe()
         return
     if args.calibrate_copy:
         import torch

@@ -10,11 +10,16 @@
 //   shared:   the same chain with weight 1 over all tokens
 //   dx[t] = sum_i dX_sorted[slot(t,i)] + router term + shared term
 //
+// In bf16, dY is never formed: the down dgrad reads G by token and applies
+// w_i after the contraction (gemm_dgrad.h), dw_i = <G W_down^T, H> comes
+// from the same accumulators, and dW_down = sum (w_i H)^T G with G's rows
+// gathered. fp32 runs the chain as written above.
+//
 // Every reduction runs in a fixed order with one writer per output (no
 // floating-point atomics), so the gradients are deterministic. In bf16 the
 // weight gradients take the transposing-LDS-read kernel (gemm_wgrad.h),
-// which reads row ranges: the token rows of dW_gate, dW_up are first copied
-// into expert order, into dY's buffer once dW_down has consumed dY.
+// which reads row ranges and gathers token rows through perm itself.
+#include "gemm_dgrad.h"
 #include "gemm_launch.h"
 #include "gemm_wgrad.h"
 
@@ -278,6 +283,71 @@ __global__ __launch_bounds__(kRowThreads) void router_reduce_kernel(
   }
 }
 
+// bf16 path, before the down dgrad: the combine weight of each sorted
+// row's slot (ws[r] = w[perm[r]]), the zero row the weight-gradient loads
+// read past a group's end, and the router transposed for dx (wrT[e][j] =
+// wr[j][e], so that its columns are contiguous rows).
+__global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(
+    int64_t rows, const int32_t* __restrict__ perm, const float* __restrict__ w,
+    float* __restrict__ ws, float* __restrict__ zero_row, int zero_n, const float* __restrict__ wr,
+    int d, int E, float* __restrict__ wrT) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kRowThreads;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
+  for (int64_t i = i0; i < zero_n; i += stride) zero_row[i] = 0.0f;
+  const int64_t dE = static_cast<int64_t>(d) * E;
+  for (int64_t i = i0; i < dE; i += stride) {
+    const int64_t e = i / d, j = i % d;
+    wrT[i] = wr[j * E + e];
+  }
+  for (int64_t r = i0; r < rows; r += stride) ws[r] = w[perm[r]];
+}
+
+// bf16 path: dl per slot from the down dgrad's dw parts (by sorted row).
+// One thread per token: dw_i = sum of the d_hidden slices' parts in slice
+// order (0 for a slot capacity routing dropped: its y is 0), then dl_i =
+// w_i (dw_i - sum_j w_j dw_j) with the sum taken in rank order. K = k <= 8
+// issues all of a token's loads of one kind before using them.
+template <int K>
+__global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
+    int64_t ntok, int k, int nparts, int64_t rows, const float* __restrict__ dwp,
+    const float* __restrict__ w, const int32_t* __restrict__ inv_perm, float* __restrict__ dl) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
+  if (t >= ntok) return;
+  if constexpr (K > 0) {
+    int64_t r[K];
+    float wv[K], dw[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      r[i] = inv_perm[t * K + i];
+      wv[i] = w[t * K + i];
+      dw[i] = 0.0f;
+    }
+    for (int q = 0; q < nparts; ++q) {
+      float v[K];
+#pragma unroll
+      for (int i = 0; i < K; ++i) v[i] = r[i] >= 0 ? dwp[q * rows + r[i]] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) dw[i] += v[i];
+    }
+    float sum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) sum = __builtin_fmaf(wv[i], dw[i], sum);
+#pragma unroll
+    for (int i = 0; i < K; ++i) dl[t * K + i] = wv[i] * (dw[i] - sum);
+  } else {
+    auto dw_of = [&](int i) {
+      const int64_t r = inv_perm[t * k + i];
+      float v = 0.0f;
+      if (r >= 0)
+        for (int q = 0; q < nparts; ++q) v += dwp[q * rows + r];
+      return v;
+    };
+    float sum = 0.0f;
+    for (int i = 0; i < k; ++i) sum = __builtin_fmaf(w[t * k + i], dw_of(i), sum);
+    for (int i = 0; i < k; ++i) dl[t * k + i] = w[t * k + i] * (dw_of(i) - sum);
+  }
+}
+
 // dx[t] = sum_i dX_sorted[slot(t,i)] + sum_i dl_i W_r[:, e_i] + dx_shared[t].
 // wrT[e][j] = wr[j][e]: the router columns as contiguous rows, so the
 // router term of dx reads 16- or 32-byte pieces instead of strided floats.
@@ -441,7 +511,9 @@ __global__ __launch_bounds__(kRowThreads) void fill_zero_kernel(float* __restric
 }
 
 struct BwdLayout {
-  size_t dY, dl, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, tiles256, total;
+  // dY holds dY [S][d] (fp32) or w H [S][h] (bf16); dwp the bf16 dw parts,
+  // wsr the bf16 combine weights by sorted row
+  size_t dY, dl, dwp, wsr, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, tiles256, total;
   int ks_sd, ks_sgu;
 };
 
@@ -464,8 +536,10 @@ BwdLayout bwd_layout(const moe_problem& p) {
   L.ks_sd = hs ? split_count(p.tokens, static_cast<int>((hs / 128) * (d / 128))) : 0;
   L.ks_sgu = hs ? split_count(p.tokens, static_cast<int>((d / 128) * (2 * hs / 128))) : 0;
   size_t o = 0;
-  L.dY = o;       o = align_up(o + S * d * es, 256);
+  L.dY = o;       o = align_up(o + S * (p.dtype == MOE_BF16 ? h : d) * es, 256);
   L.dl = o;       o = align_up(o + S * 4, 256);
+  L.dwp = o;      o = align_up(o + ((h + 127) / 128) * S * 4, 256);
+  L.wsr = o;      o = align_up(o + S * 4, 256);
   L.dAB = o;      o = align_up(o + S * 2 * h * es, 256);
   L.dXs = o;      o = align_up(o + S * d * es, 256);
   L.rpart = o;    o = align_up(o + max_tiles * d * 4, 256);
@@ -505,10 +579,47 @@ void wgrad(const char* name, const WgradArgs& a, int groups, const void* zero, h
              dim3(256), 0, s, a);
 }
 
+// a15: dX_sorted = dA W_gate^T + dB W_up^T, on the 256-row tile list
+// (built by the caller when retile_rows(p) or when the bf16 down dgrad ran)
+// or the caller's block_m list.
 template <typename T>
-void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
-                  const void* saved_ab, const void* dY, void* dAB, void* dXs, void* tiles256,
-                  hipStream_t s) {
+void gate_up_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
+                   const void* dAB, void* dXs, int32_t* t256, bool t256_built, hipStream_t s) {
+  const int64_t S = p.tokens * p.top_k;
+  const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
+  const int d = p.d_model, h = p.d_hidden;
+  GemmArgs b{};
+  b.a = dAB;
+  b.lda = 2 * static_cast<int64_t>(h);
+  b.b = w.w_gate;  // [E][d][h]: row n = model unit, K = h contiguous
+  b.b_group_stride = static_cast<int64_t>(d) * h;
+  b.ldb = h;
+  b.b2 = w.w_up;
+  b.b2_group_stride = static_cast<int64_t>(d) * h;
+  b.ksplit = h;
+  b.N = d;
+  b.K = 2 * h;
+  b.tiles = r.tiles;
+  b.num_tiles = r.num_tiles;
+  b.c = dXs;
+  b.ldc = d;
+  if (retile_rows(p) && wide_fits<T>(b)) {
+    // 256-row tiles on the wide engine (K = 2h, N = d_model)
+    const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
+    if (!t256_built)
+      (void)launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
+    b.tiles = t256 + 4;
+    b.num_tiles = t256;
+    grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, kRetileBm, mt256, s);
+  } else {
+    grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, p.block_m, max_tiles, s);
+  }
+}
+
+// fp32 a13: dH = dY W_down^T and the SwiGLU backward into dA|dB.
+template <typename T>
+void down_dgrad_dy(const moe_problem& p, const moe_weights& w, const moe_routing& r,
+                   const void* saved_ab, const void* dY, void* dAB, hipStream_t s) {
   const int64_t S = p.tokens * p.top_k;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
   const int d = p.d_model, h = p.d_hidden;
@@ -528,33 +639,32 @@ void routed_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing&
   a.sb = const_cast<T*>(static_cast<const T*>(saved_ab) + h);
   a.lds = 2 * static_cast<int64_t>(h);
   grouped_gemm<T, false, kEpiSwigluBwd>("bwd_down_dgrad", a, p.block_m, max_tiles, s);
+}
 
-  GemmArgs b{};
-  b.a = dAB;
-  b.lda = 2 * static_cast<int64_t>(h);
-  b.b = w.w_gate;  // [E][d][h]: row n = model unit, K = h contiguous
-  b.b_group_stride = static_cast<int64_t>(d) * h;
-  b.ldb = h;
-  b.b2 = w.w_up;
-  b.b2_group_stride = static_cast<int64_t>(d) * h;
-  b.ksplit = h;
-  b.N = d;
-  b.K = 2 * h;
-  b.tiles = r.tiles;
-  b.num_tiles = r.num_tiles;
-  b.c = dXs;
-  b.ldc = d;
-  if (retile_rows(p) && wide_fits<T>(b)) {
-    // 256-row tiles on the wide engine (K = 2h, N = d_model)
-    int32_t* t256 = static_cast<int32_t*>(tiles256);
-    const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
-    (void)launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
-    b.tiles = t256 + 4;
-    b.num_tiles = t256;
-    grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, kRetileBm, mt256, s);
-  } else {
-    grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, p.block_m, max_tiles, s);
-  }
+// bf16 a11 + a13 (gemm_dgrad.h) over the 256-row list t256 (mt256 entries
+// at most): dA|dB, w H into hw, and the dw parts.
+void down_dgrad_fused(const moe_problem& p, const moe_weights& w, const moe_routing& r,
+                      const void* saved_ab, const void* grad_out, const float* wsr, bf16_t* hw,
+                      void* dAB, float* dwp, const int32_t* t256, int64_t mt256, hipStream_t s) {
+  DgradArgs a{};
+  a.g = static_cast<const bf16_t*>(grad_out);
+  a.perm = r.perm;
+  a.topk = p.top_k;
+  a.w = static_cast<const bf16_t*>(w.w_down);
+  a.sab = static_cast<const bf16_t*>(saved_ab);
+  a.ws = wsr;
+  a.dab = static_cast<bf16_t*>(dAB);
+  a.hw = hw;
+  a.dwp = dwp;
+  a.rows = p.tokens * p.top_k;
+  a.d = p.d_model;
+  a.h = p.d_hidden;
+  const int64_t work = mt256 * (p.d_hidden / 128);
+  if (work <= 0) return;
+  const int slots = persistent_slots(reinterpret_cast<const void*>(&down_dgrad_kernel), 512);
+  const unsigned grid = static_cast<unsigned>(work < slots ? work : slots);
+  MOE_LAUNCH("bwd_down_dgrad", down_dgrad_kernel, dim3(grid), dim3(512), 0, s, a, t256 + 4, t256,
+             static_cast<int>(work));
 }
 
 template <typename T>
@@ -573,10 +683,18 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   T* dAB = reinterpret_cast<T*>(W + L.dAB);
   T* dXs = reinterpret_cast<T*>(W + L.dXs);
   float* rpart = reinterpret_cast<float*>(W + L.rpart);
-  // Zero row the bf16 weight-gradient loads read past a group's end.
+  // Zero row the bf16 weight-gradient loads read past a group's end (and,
+  // in bf16, the combine weights by sorted row for the down dgrad).
   const void* zero_row = W + L.zero;
-  if (std::is_same<T, bf16_t>::value)
-    zero(reinterpret_cast<float*>(W + L.zero), kTrZeroBytes / 4, s);
+  float* wsr = reinterpret_cast<float*>(W + L.wsr);
+  if (std::is_same<T, bf16_t>::value) {
+    int64_t blocks = (S + kRowThreads - 1) / kRowThreads;
+    blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
+    MOE_LAUNCH("bwd_prep", bwd_prep_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRowThreads),
+               0, s, S, r.perm, r.topk_w, wsr, reinterpret_cast<float*>(W + L.zero),
+               static_cast<int>(kTrZeroBytes / 4), w.w_router, d, E,
+               reinterpret_cast<float*>(W + L.wrT));
+  }
   const int64_t row_blocks = (T_ + kRowThreads / 64 - 1) / (kRowThreads / 64);
 
   T* dxs = nullptr;
@@ -585,48 +703,94 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   // the side stream beside the routed path (each lambda's stream parameter
   // is the `s` its launches use).
   auto routed_bwd = [&](hipStream_t s) {
-    // a11: combine backward and per-slot router gradient
-    const T* g_t = static_cast<const T*>(grad_out);
-    const T* y_t = static_cast<const T*>(y_sorted);
+    const void* sab = SV + F.sv_ab;
+    int32_t* t256 = reinterpret_cast<int32_t*>(W + L.tiles256);
+    bool t256_built = false;
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      // a11 + a13: the down dgrad reads G by token and yields dA|dB, w H
+      // and the combine weights' gradient parts; then dl per slot
+      const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + E;
+      (void)launch_retile(r.expert_offsets, E, kRetileBm, p.capacity, t256 + 4, t256, s);
+      t256_built = true;
+      float* dwp = reinterpret_cast<float*>(W + L.dwp);
+      down_dgrad_fused(p, w, r, sab, grad_out, wsr, dY, dAB, dwp, t256, mt256, s);
+      const dim3 dl_grid(static_cast<unsigned>((T_ + kRowThreads - 1) / kRowThreads));
+#define MOE_DL_K(KK)                                                                         \
+  case KK:                                                                                   \
+    MOE_LAUNCH("bwd_router_dl", router_dl_kernel<KK>, dl_grid, dim3(kRowThreads), 0, s, T_, \
+               k, h / 128, S, dwp, r.topk_w, r.inv_perm, dl);                                \
+    break;
+      switch (k) {
+        MOE_DL_K(1) MOE_DL_K(2) MOE_DL_K(3) MOE_DL_K(4) MOE_DL_K(5) MOE_DL_K(6) MOE_DL_K(7)
+        MOE_DL_K(8)
+        default:
+          MOE_LAUNCH("bwd_router_dl", router_dl_kernel<0>, dl_grid, dim3(kRowThreads), 0, s, T_, k,
+                     h / 128, S, dwp, r.topk_w, r.inv_perm, dl);
+      }
+#undef MOE_DL_K
+    } else {
+      // a11: combine backward and per-slot router gradient
+      const T* g_t = static_cast<const T*>(grad_out);
+      const T* y_t = static_cast<const T*>(y_sorted);
 #define MOE_CB_K(KK)                                                                          \
   case KK:                                                                                    \
     MOE_LAUNCH("bwd_combine", (combine_bwd_k_kernel<T, KK>),                                  \
                dim3(static_cast<unsigned>(row_blocks)), dim3(kRowThreads), 0, s, T_, d, g_t,  \
                y_t, r.topk_w, r.inv_perm, dY, dl);                                            \
     break;
-    switch (k) {
-      MOE_CB_K(1) MOE_CB_K(2) MOE_CB_K(3) MOE_CB_K(4) MOE_CB_K(5) MOE_CB_K(6) MOE_CB_K(7)
-      MOE_CB_K(8)
-      default:
-        MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
-                   dim3(kRowThreads), 0, s, T_, k, d, g_t, y_t, r.topk_w, r.inv_perm, dY, dl);
-    }
+      switch (k) {
+        MOE_CB_K(1) MOE_CB_K(2) MOE_CB_K(3) MOE_CB_K(4) MOE_CB_K(5) MOE_CB_K(6) MOE_CB_K(7)
+        MOE_CB_K(8)
+        default:
+          MOE_LAUNCH("bwd_combine", combine_bwd_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
+                     dim3(kRowThreads), 0, s, T_, k, d, g_t, y_t, r.topk_w, r.inv_perm, dY, dl);
+      }
 #undef MOE_CB_K
+      // a13: down dgrad from dY
+      down_dgrad_dy<T>(p, w, r, sab, dY, dAB, s);
+    }
     // a12: router weight gradient (tile partials, then a per-expert ordered sum)
     MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
                dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
                r.expert_offsets, E, p.block_m, rpart);
     MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
                r.expert_offsets, E, p.block_m, d, g.w_router);
-    // a13 + a15: dgrad GEMMs
-    const void* sab = SV + F.sv_ab;
-    routed_dgrad<T>(p, w, r, sab, dY, dAB, dXs, W + L.tiles256, s);
+    // a15: gate/up dgrad
+    gate_up_dgrad<T>(p, w, r, dAB, dXs, t256, t256_built, s);
     // a14: per-expert weight gradients, K = the expert's rows
     {
       WgradArgs a{};
-      a.a = SV + F.sv_h;
-      a.lda = h;
-      a.b = dY;
-      a.ldb = d;
       a.M = h;
       a.N = d;
       a.row_offsets = r.expert_offsets;
       a.cap = p.capacity;
       a.c = g.w_down;
-      a.nsplit = d;
-      a.ldc = d;
       a.c_group_stride = static_cast<int64_t>(h) * d;
-      wgrad<T, false, false>("bwd_wgrad_down", a, E, zero_row, s);
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        // dW_down[e]^T = sum over rows of G[token]^T (w H): G gathered as
+        // the M side, stored transposed into [h][d]
+        a.a = grad_out;
+        a.lda = d;
+        a.perm = r.perm;
+        a.topk = k;
+        a.rows_total = S;
+        a.b = dY;  // w H
+        a.ldb = h;
+        a.M = d;
+        a.N = h;
+        a.nsplit = h;
+        a.ldc = d;
+        a.trans_c = 1;
+        wgrad<T, true, false>("bwd_wgrad_down", a, E, zero_row, s);
+      } else {
+        a.a = SV + F.sv_h;
+        a.lda = h;
+        a.b = dY;
+        a.ldb = d;
+        a.nsplit = d;
+        a.ldc = d;
+        wgrad<T, false, false>("bwd_wgrad_down", a, E, zero_row, s);
+      }
       WgradArgs b{};
       b.a = x;
       b.lda = d;
@@ -735,8 +899,9 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   }
   // dx: gather-sum of the routed input gradients plus the router and shared terms
   float* wrT = reinterpret_cast<float*>(W + L.wrT);
-  MOE_LAUNCH("bwd_router_transpose", router_transpose_kernel, dim3((d + 31) / 32, (E + 31) / 32),
-             dim3(256), 0, s, w.w_router, d, E, wrT);
+  if (!std::is_same<T, bf16_t>::value)  // bf16: bwd_prep wrote it
+    MOE_LAUNCH("bwd_router_transpose", router_transpose_kernel, dim3((d + 31) / 32, (E + 31) / 32),
+               dim3(256), 0, s, w.w_router, d, E, wrT);
   const T* dxs_t = static_cast<const T*>(dxs);
   T* gx = static_cast<T*>(grad_x);
 #define MOE_DX_K(KK)                                                                          \

@@ -495,6 +495,7 @@ struct WgradArgs {
   int nsplit;
   int64_t ldc;
   int64_t c_group_stride;
+  int trans_c;     // bf16 kernel: store C^T, element (m, n) at c + n * ldc + m (no c2)
 };
 
 template <typename T>

@@ -304,6 +304,12 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad_tr_kernel(const WgradArgs p,
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int n = b_col + wn * 64 + j * 32 + 8 * rr + 4 * g;
+        if (p.trans_c) {
+          // C^T: the 32 lanes of a column n write 32 consecutive floats.
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cg[static_cast<int64_t>(n + q) * p.ldc + m] = acc[i][j][4 * rr + q];
+          continue;
+        }
         float* dst = n < p.nsplit ? cg + m * p.ldc + n : cg2 + m * p.ldc + (n - p.nsplit);
         *reinterpret_cast<float4*>(dst) =
             make_float4(acc[i][j][4 * rr], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2],
@@ -312,15 +318,17 @@ __global__ __launch_bounds__(Cfg::NT) void wgrad_tr_kernel(const WgradArgs p,
   }
 }
 
-// Launch over (group, M tile, N tile); M a multiple of 128 (256 taken when it
-// divides), N a multiple of 128; `zero` a kTrZeroBytes zero buffer.
+// Launch over (group, M tile, N tile); M a multiple of 128 (256-row M tiles
+// taken when they divide M and still give a workgroup to every CU), N a
+// multiple of 128; `zero` a kTrZeroBytes zero buffer.
 // kGather: a.perm (a.rows_total entries, at least one) maps rows to slots,
 // token = slot / a.topk.
 template <bool kDense, bool kGather = false>
 void wgrad_tr(const char* name, const WgradArgs& a, int groups, const bf16_t* zero,
               hipStream_t s) {
   if (kGather && a.rows_total < 1) return;
-  if (a.M % 256 == 0) {
+  if (a.M % 256 == 0 &&
+      static_cast<int64_t>(groups) * (a.M / 256) * (a.N / 128) >= cu_count()) {
     using Cfg = TrCfg<256, 3>;
     const int64_t blocks = static_cast<int64_t>(groups) * (a.M / 256) * (a.N / 128);
     if (blocks <= 0) return;

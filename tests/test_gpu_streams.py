@@ -166,5 +166,6 @@ def test_kernel_timer_mode_gives_the_same_bits():
     for a, b in zip(plain, timed):
         assert bits_equal(a, b)
     for name in ("route", "gemm_gate_up", "gemm_down", "shared_gate_up", "shared_down", "combine",
-                 "bwd_combine", "bwd_shared_down_dgrad", "bwd_wgrad_gate_up", "bwd_dx"):
+                 "bwd_down_dgrad", "bwd_router_dl", "bwd_shared_down_dgrad", "bwd_wgrad_gate_up",
+                 "bwd_dx"):
         assert name in kern and kern[name]["count"] >= 1, name
