@@ -17,6 +17,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+# Measurement probe of the wide GEMM engine's stage loop (bench.py
+# --stage-probe); a library of its own, not part of libmoe.
+PROBE_SRC = os.path.join(CSRC, "probe", "stage_probe.hip")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -36,6 +40,8 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if src == PROBE_SRC:
+        obj = os.path.join(BUILD, "probe_" + os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC] + FLAGS + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -44,20 +50,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
-    """Compiles every source and links libmoe.so (always rebuilds)."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}"] + objs + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8, verbose: bool = True) -> str:
+    """Compiles every source, links libmoe.so and the stage-loop probe
+    library (always rebuilds)."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources() + [PROBE_SRC]
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {PROBE_LIB}", file=sys.stderr)
     return LIB
 
 

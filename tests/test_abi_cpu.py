@@ -32,6 +32,22 @@ def test_exports_every_declared_symbol():
     assert "gfx950" in B.moe_version()
 
 
+def test_stage_probe_library_loads():
+    """The wide engine's stage-loop probe (bench.py --stage-probe) is a
+    library of its own, built beside libmoe; it rejects bad configurations
+    on the host before touching a GPU."""
+    lib = ctypes.CDLL(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "libmoe_probe.so"))
+    fn = lib.moe_stage_probe
+    fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    ms = ctypes.c_float(0.0)
+    assert fn(7, 4096, 0, 256, 16, 1, ctypes.byref(ms)) == -1      # no such mode
+    assert fn(3, 100, 0, 256, 16, 1, ctypes.byref(ms)) == -1       # region under one tile
+    assert fn(3, (1 << 20) + 1, 0, 256, 16, 1, ctypes.byref(ms)) == -1
+    assert fn(3, 4096, 0, 0, 16, 1, ctypes.byref(ms)) == -1
+    assert fn(3, 4096, 0, 256, 16, 1, None) == -1
+
+
 def test_param_count_and_tiles():
     p = Problem(4096, 8, 2, 512, 1024, 0, "fp32", 64)
     assert B.moe_param_count(p) == 12587008  # gpu_nn.json, moe suite, "params"
