@@ -52,6 +52,10 @@ struct V16<bf16_t> {
     o[0] = bf16lo(v.x); o[1] = bf16hi(v.x); o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
     o[4] = bf16lo(v.z); o[5] = bf16hi(v.z); o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
   }
+  __device__ static void unpack(const u32x4& v, float* o) {
+    o[0] = bf16lo(v.x); o[1] = bf16hi(v.x); o[2] = bf16lo(v.y); o[3] = bf16hi(v.y);
+    o[4] = bf16lo(v.z); o[5] = bf16hi(v.z); o[6] = bf16lo(v.w); o[7] = bf16hi(v.w);
+  }
   __device__ static void store_nt(bf16_t* p, const float* o) {
     u32x4 v;
     v.x = pack_bf16x2(o[0], o[1]); v.y = pack_bf16x2(o[2], o[3]);
@@ -72,6 +76,10 @@ struct V16<float> {
   __device__ static void load_nt(const float* p, float* o) {
     const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
     o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+  }
+  __device__ static void unpack(const u32x4& v, float* o) {
+    o[0] = __uint_as_float(v.x); o[1] = __uint_as_float(v.y);
+    o[2] = __uint_as_float(v.z); o[3] = __uint_as_float(v.w);
   }
   __device__ static void store_nt(float* p, const float* o) {
     const f32x4_t v = {o[0], o[1], o[2], o[3]};
@@ -302,7 +310,9 @@ __global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(
   for (int64_t r = i0; r < rows; r += stride) ws[r] = w[perm[r]];
 }
 
-// bf16 path: dl per slot from the down dgrad's dw parts (by sorted row).
+// bf16 path: dl per slot from the down dgrad's dw parts (by sorted row),
+// written by slot (dl) and, for kept slots, by sorted row (dls, which the
+// gate/up dgrad's epilogue scales the router column by).
 // One thread per token: dw_i = sum of the d_hidden slices' parts in slice
 // order (0 for a slot capacity routing dropped: its y is 0), then dl_i =
 // w_i (dw_i - sum_j w_j dw_j) with the sum taken in rank order. K = k <= 8
@@ -310,7 +320,8 @@ __global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(
 template <int K>
 __global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
     int64_t ntok, int k, int nparts, int64_t rows, const float* __restrict__ dwp,
-    const float* __restrict__ w, const int32_t* __restrict__ inv_perm, float* __restrict__ dl) {
+    const float* __restrict__ w, const int32_t* __restrict__ inv_perm, float* __restrict__ dl,
+    float* __restrict__ dls) {
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
   if (t >= ntok) return;
   if constexpr (K > 0) {
@@ -333,7 +344,11 @@ __global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
 #pragma unroll
     for (int i = 0; i < K; ++i) sum = __builtin_fmaf(wv[i], dw[i], sum);
 #pragma unroll
-    for (int i = 0; i < K; ++i) dl[t * K + i] = wv[i] * (dw[i] - sum);
+    for (int i = 0; i < K; ++i) {
+      const float v = wv[i] * (dw[i] - sum);
+      dl[t * K + i] = v;
+      if (r[i] >= 0) dls[r[i]] = v;
+    }
   } else {
     auto dw_of = [&](int i) {
       const int64_t r = inv_perm[t * k + i];
@@ -344,7 +359,12 @@ __global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
     };
     float sum = 0.0f;
     for (int i = 0; i < k; ++i) sum = __builtin_fmaf(w[t * k + i], dw_of(i), sum);
-    for (int i = 0; i < k; ++i) dl[t * k + i] = w[t * k + i] * (dw_of(i) - sum);
+    for (int i = 0; i < k; ++i) {
+      const float v = w[t * k + i] * (dw_of(i) - sum);
+      dl[t * k + i] = v;
+      const int64_t r = inv_perm[t * k + i];
+      if (r >= 0) dls[r] = v;
+    }
   }
 }
 
@@ -368,7 +388,9 @@ __global__ __launch_bounds__(256) void router_transpose_kernel(const float* __re
   }
 }
 
-template <typename T>
+// kKeptRouter: the gate/up dgrad already added the router term to the rows
+// of kept slots, so only dropped slots (capacity routing) add it here.
+template <typename T, bool kKeptRouter>
 __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
     int64_t ntok, int k, int d, int E, const T* __restrict__ dxs, const int32_t* __restrict__ inv_perm,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
@@ -393,6 +415,11 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
 #pragma unroll
         for (int q = 0; q < N; ++q) v[q] = 0.0f;
       }
+      if (kKeptRouter && slot >= 0) {
+#pragma unroll
+        for (int q = 0; q < N; ++q) acc[q] += v[q];
+        continue;
+      }
 #pragma unroll
       for (int q = 0; q < N; q += 4) {
         const float4 w4 = *reinterpret_cast<const float4*>(wrT + static_cast<int64_t>(e) * d + c + q);
@@ -416,7 +443,7 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_kernel(
 // expert-row and router-row loads of a piece (and the shared row's) are
 // issued before any is used: one memory latency per token instead of 2K
 // dependent ones. Same arithmetic and order as dx_gather_kernel.
-template <typename T, int K>
+template <typename T, int K, bool kKeptRouter>
 __global__ __launch_bounds__(kRowThreads) void dx_gather_k_kernel(
     int64_t ntok, int d, const T* __restrict__ dxs, const int32_t* __restrict__ inv_perm,
     const int32_t* __restrict__ topk_idx, const float* __restrict__ dl,
@@ -438,31 +465,48 @@ __global__ __launch_bounds__(kRowThreads) void dx_gather_k_kernel(
     li[i] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_l), i));
   }
   for (int c = lane * N; c < d; c += 64 * N) {
-    float v[K][N], wv[K][N], sv[N];
+    // The K rows and the shared row are loaded raw, all before any is used
+    // (16 bytes = 4 registers each; converted to fp32 they took twice that
+    // and held the kernel to 3 waves per SIMD); then the router terms.
+    u32x4 raw[K], sraw = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      if (slot[i] >= 0) {
-        V16<T>::load_nt(dxs + slot[i] * d + c, v[i]);
-      } else {
-        // dropped by capacity routing: only the router term
-#pragma unroll
-        for (int q = 0; q < N; ++q) v[i][q] = 0.0f;
-      }
-#pragma unroll
-      for (int q = 0; q < N; q += 4) {
-        const float4 w4 = *reinterpret_cast<const float4*>(wrT + static_cast<int64_t>(e[i]) * d + c + q);
-        wv[i][q] = w4.x; wv[i][q + 1] = w4.y; wv[i][q + 2] = w4.z; wv[i][q + 3] = w4.w;
-      }
-    }
-    if (dx_shared) V16<T>::load_nt(dx_shared + t * d + c, sv);
+    for (int i = 0; i < K; ++i)
+      raw[i] = slot[i] >= 0
+                   ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dxs + slot[i] * d + c))
+                   : u32x4{0u, 0u, 0u, 0u};  // dropped by capacity routing: only the router term
+    if (dx_shared) sraw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dx_shared + t * d + c));
     float acc[N];
 #pragma unroll
     for (int q = 0; q < N; ++q) acc[q] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < K; ++i)
+    for (int i = 0; i < K; ++i) {
+      float v[N];
+      V16<T>::unpack(raw[i], v);
 #pragma unroll
-      for (int q = 0; q < N; ++q) acc[q] += __builtin_fmaf(li[i], wv[i][q], v[i][q]);
+      for (int q = 0; q < N; ++q) acc[q] += v[q];
+    }
+    auto router_term = [&](int i) {
+#pragma unroll
+      for (int q = 0; q < N; q += 4) {
+        const float4 w4 = *reinterpret_cast<const float4*>(wrT + static_cast<int64_t>(e[i]) * d + c + q);
+        acc[q] = __builtin_fmaf(li[i], w4.x, acc[q]);
+        acc[q + 1] = __builtin_fmaf(li[i], w4.y, acc[q + 1]);
+        acc[q + 2] = __builtin_fmaf(li[i], w4.z, acc[q + 2]);
+        acc[q + 3] = __builtin_fmaf(li[i], w4.w, acc[q + 3]);
+      }
+    };
+    if (kKeptRouter) {
+      // only slots capacity routing dropped (rare): one at a time
+#pragma unroll 1
+      for (int i = 0; i < K; ++i)
+        if (slot[i] < 0) router_term(i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) router_term(i);
+    }
     if (dx_shared) {
+      float sv[N];
+      V16<T>::unpack(sraw, sv);
 #pragma unroll
       for (int q = 0; q < N; ++q) acc[q] += sv[q];
     }
@@ -512,8 +556,10 @@ __global__ __launch_bounds__(kRowThreads) void fill_zero_kernel(float* __restric
 
 struct BwdLayout {
   // dY holds dY [S][d] (fp32) or w H [S][h] (bf16); dwp the bf16 dw parts,
-  // wsr the bf16 combine weights by sorted row
-  size_t dY, dl, dwp, wsr, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, tiles256, total;
+  // wsr the bf16 combine weights and dls its router-logit gradients by
+  // sorted row
+  size_t dY, dl, dls, dwp, wsr, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, tiles256,
+      total;
   int ks_sd, ks_sgu;
 };
 
@@ -540,6 +586,7 @@ BwdLayout bwd_layout(const moe_problem& p) {
   L.dl = o;       o = align_up(o + S * 4, 256);
   L.dwp = o;      o = align_up(o + ((h + 127) / 128) * S * 4, 256);
   L.wsr = o;      o = align_up(o + S * 4, 256);
+  L.dls = o;      o = align_up(o + S * 4, 256);
   L.dAB = o;      o = align_up(o + S * 2 * h * es, 256);
   L.dXs = o;      o = align_up(o + S * d * es, 256);
   L.rpart = o;    o = align_up(o + max_tiles * d * 4, 256);
@@ -581,10 +628,13 @@ void wgrad(const char* name, const WgradArgs& a, int groups, const void* zero, h
 
 // a15: dX_sorted = dA W_gate^T + dB W_up^T, on the 256-row tile list
 // (built by the caller when retile_rows(p) or when the bf16 down dgrad ran)
-// or the caller's block_m list.
+// or the caller's block_m list. With dls (dl by sorted row) and wrT (the
+// router transposed), the wide engine also adds each row's router term
+// dl * W_r[:, e] before rounding; returns whether it did.
 template <typename T>
-void gate_up_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
-                   const void* dAB, void* dXs, int32_t* t256, bool t256_built, hipStream_t s) {
+bool gate_up_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing& r,
+                   const void* dAB, void* dXs, int32_t* t256, bool t256_built, const float* dls,
+                   const float* wrT, hipStream_t s) {
   const int64_t S = p.tokens * p.top_k;
   const int64_t max_tiles = (S + p.block_m - 1) / p.block_m + p.experts;
   const int d = p.d_model, h = p.d_hidden;
@@ -603,17 +653,24 @@ void gate_up_dgrad(const moe_problem& p, const moe_weights& w, const moe_routing
   b.num_tiles = r.num_tiles;
   b.c = dXs;
   b.ldc = d;
-  if (retile_rows(p) && wide_fits<T>(b)) {
+  if ((retile_rows(p) || (t256_built && p.block_m == kRetileBm)) && wide_fits<T>(b)) {
     // 256-row tiles on the wide engine (K = 2h, N = d_model)
     const int64_t mt256 = (S + kRetileBm - 1) / kRetileBm + p.experts;
     if (!t256_built)
       (void)launch_retile(r.expert_offsets, p.experts, kRetileBm, p.capacity, t256 + 4, t256, s);
     b.tiles = t256 + 4;
     b.num_tiles = t256;
+    if (dls && wrT) {
+      b.rdl = dls;
+      b.rw = wrT;
+      wide_gemm<false, kEpiStoreRouter, false>("bwd_gate_up_dgrad", b, mt256, s);
+      return true;
+    }
     grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, kRetileBm, mt256, s);
   } else {
     grouped_gemm<T, false, kEpiStore>("bwd_gate_up_dgrad", b, p.block_m, max_tiles, s);
   }
+  return false;
 }
 
 // fp32 a13: dH = dY W_down^T and the SwiGLU backward into dA|dB.
@@ -687,6 +744,9 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   // in bf16, the combine weights by sorted row for the down dgrad).
   const void* zero_row = W + L.zero;
   float* wsr = reinterpret_cast<float*>(W + L.wsr);
+  float* dls = reinterpret_cast<float*>(W + L.dls);
+  float* wrT = reinterpret_cast<float*>(W + L.wrT);
+  bool router_folded = false;
   if (std::is_same<T, bf16_t>::value) {
     int64_t blocks = (S + kRowThreads - 1) / kRowThreads;
     blocks = blocks < 1 ? 1 : (blocks > 2048 ? 2048 : blocks);
@@ -718,14 +778,14 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
 #define MOE_DL_K(KK)                                                                         \
   case KK:                                                                                   \
     MOE_LAUNCH("bwd_router_dl", router_dl_kernel<KK>, dl_grid, dim3(kRowThreads), 0, s, T_, \
-               k, h / 128, S, dwp, r.topk_w, r.inv_perm, dl);                                \
+               k, h / 128, S, dwp, r.topk_w, r.inv_perm, dl, dls);                                \
     break;
       switch (k) {
         MOE_DL_K(1) MOE_DL_K(2) MOE_DL_K(3) MOE_DL_K(4) MOE_DL_K(5) MOE_DL_K(6) MOE_DL_K(7)
         MOE_DL_K(8)
         default:
           MOE_LAUNCH("bwd_router_dl", router_dl_kernel<0>, dl_grid, dim3(kRowThreads), 0, s, T_, k,
-                     h / 128, S, dwp, r.topk_w, r.inv_perm, dl);
+                     h / 128, S, dwp, r.topk_w, r.inv_perm, dl, dls);
       }
 #undef MOE_DL_K
     } else {
@@ -755,8 +815,9 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
                r.expert_offsets, E, p.block_m, rpart);
     MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
                r.expert_offsets, E, p.block_m, d, g.w_router);
-    // a15: gate/up dgrad
-    gate_up_dgrad<T>(p, w, r, dAB, dXs, t256, t256_built, s);
+    // a15: gate/up dgrad (bf16: with the router term of each kept slot)
+    router_folded = gate_up_dgrad<T>(p, w, r, dAB, dXs, t256, t256_built, t256_built ? dls : nullptr,
+                                     t256_built ? wrT : nullptr, s);
     // a14: per-expert weight gradients, K = the expert's rows
     {
       WgradArgs a{};
@@ -898,7 +959,6 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     routed_bwd(s);
   }
   // dx: gather-sum of the routed input gradients plus the router and shared terms
-  float* wrT = reinterpret_cast<float*>(W + L.wrT);
   if (!std::is_same<T, bf16_t>::value)  // bf16: bwd_prep wrote it
     MOE_LAUNCH("bwd_router_transpose", router_transpose_kernel, dim3((d + 31) / 32, (E + 31) / 32),
                dim3(256), 0, s, w.w_router, d, E, wrT);
@@ -906,16 +966,27 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   T* gx = static_cast<T*>(grad_x);
 #define MOE_DX_K(KK)                                                                          \
   case KK:                                                                                    \
-    MOE_LAUNCH("bwd_dx", (dx_gather_k_kernel<T, KK>), dim3(static_cast<unsigned>(row_blocks)), \
-               dim3(kRowThreads), 0, s, T_, d, dXs, r.inv_perm, r.topk_idx, dl, wrT, dxs_t, gx); \
+    if (router_folded)                                                                        \
+      MOE_LAUNCH("bwd_dx", (dx_gather_k_kernel<T, KK, true>),                                  \
+                 dim3(static_cast<unsigned>(row_blocks)), dim3(kRowThreads), 0, s, T_, d, dXs, \
+                 r.inv_perm, r.topk_idx, dl, wrT, dxs_t, gx);                                 \
+    else                                                                                      \
+      MOE_LAUNCH("bwd_dx", (dx_gather_k_kernel<T, KK, false>),                                 \
+                 dim3(static_cast<unsigned>(row_blocks)), dim3(kRowThreads), 0, s, T_, d, dXs, \
+                 r.inv_perm, r.topk_idx, dl, wrT, dxs_t, gx);                                 \
     break;
   switch (k) {
     MOE_DX_K(1) MOE_DX_K(2) MOE_DX_K(3) MOE_DX_K(4) MOE_DX_K(5) MOE_DX_K(6) MOE_DX_K(7)
     MOE_DX_K(8)
     default:
-      MOE_LAUNCH("bwd_dx", dx_gather_kernel<T>, dim3(static_cast<unsigned>(row_blocks)),
-                 dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, wrT, dxs_t,
-                 gx);
+      if (router_folded)
+        MOE_LAUNCH("bwd_dx", (dx_gather_kernel<T, true>), dim3(static_cast<unsigned>(row_blocks)),
+                   dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, wrT,
+                   dxs_t, gx);
+      else
+        MOE_LAUNCH("bwd_dx", (dx_gather_kernel<T, false>), dim3(static_cast<unsigned>(row_blocks)),
+                   dim3(kRowThreads), 0, s, T_, k, d, E, dXs, r.inv_perm, r.topk_idx, dl, wrT,
+                   dxs_t, gx);
   }
 #undef MOE_DX_K
   return hipGetLastError();

@@ -29,8 +29,9 @@ enum EpiMode {
   kEpiSwiglu = 1,    // packed gate|up columns -> c[row][j] = SiLU(gate) * up (+ saved gate, up)
   kEpiSwigluBwd = 2, // acc = dH[row][j]; with saved gate a and up b:
                      // c[row][j] = dH b SiLU'(a), c[row][h + j] = dH SiLU(a)
-  kEpiCombine = 3    // dense rows are tokens t: v = acc rounded to the storage type,
+  kEpiCombine = 3,   // dense rows are tokens t: v = acc rounded to the storage type,
                      // c[t][n] = sum_i gw[t,i] * gy[ginv[t*gk + i]][n] + v
+  kEpiStoreRouter = 4  // wide bf16 engine only: c[row][n] = acc + rdl[row] * rw[group][n]
 };
 
 // Largest top_k the fused gather-sum epilogue takes.
@@ -61,6 +62,8 @@ struct GemmArgs {
   const float* gw;          // fused combine: [M][gk] weights
   const int32_t* ginv;      // fused combine: [M][gk] sorted row of each (token, rank)
   int gk;                   // fused combine: top_k (<= kCombineMaxK)
+  const float* rdl;         // kEpiStoreRouter: per-row scale, indexed by tile row
+  const float* rw;          // kEpiStoreRouter: [groups][N] rows added, scaled by rdl
 };
 
 // Value of v once stored in T and read back.

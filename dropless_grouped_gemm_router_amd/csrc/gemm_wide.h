@@ -243,7 +243,7 @@ __device__ __forceinline__ void wide_drain32(const char* region, bf16_t* dst, in
 // and SwiGLU-backward drains skip rows past the tile's end).
 template <int kEpi>
 __device__ __forceinline__ int wide_epilogue_stores(const GemmArgs& p) {
-  return kEpi == kEpiStore ? 16 : (kEpi == kEpiSwiglu ? (p.sa ? 24 : 8) : 0);
+  return (kEpi == kEpiStore || kEpi == kEpiStoreRouter) ? 16 : (kEpi == kEpiSwiglu ? (p.sa ? 24 : 8) : 0);
 }
 
 // First wait of an item whose predecessor's epilogue issued n stores after
@@ -372,7 +372,8 @@ template <int kEpi>
 __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
                                               const f32x16_t (&acc)[WideCfg::WM_SUB][WideCfg::WN_SUB],
                                               char* region, char* comb, int row0, int rows,
-                                              int nt, int wm, int wn, int g, int r32, int lane) {
+                                              int nt, int wm, int wn, int g, int r32, int lane,
+                                              int group) {
   const int wrows = rows - wm * 64;  // rows of this wave's block that exist
   const int64_t orow = static_cast<int64_t>(row0) + wm * 64;
   bf16_t* c = static_cast<bf16_t*>(p.c);
@@ -422,11 +423,30 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
         }
       wide_drain_swiglu_bwd(p, region, orow, nt * WideCfg::BN + wn * 128 + h * 32, wrows, lane);
     }
-  } else if (kEpi == kEpiStore) {
+  } else if (kEpi == kEpiStore || kEpi == kEpiStoreRouter) {
     // Four passes of 32 rows x 64 columns (MFMA tile row i, tiles j = 2h,
     // 2h + 1) through the first 4 KiB of the region: the wave's 4 KiB share
     // of the buffer's A half, so a stage buffer's B half survives the
     // epilogue (wide_gemm_kernel keeps the weights of K = 128 GEMMs).
+    // kEpiStoreRouter first adds rdl[row] * rw[group][n] in fp32: the
+    // lane's two row scales and its 64 columns of rw are loaded before any
+    // store (a row past the tile's end takes the last row's scale, so it
+    // still repeats that row's bits), so the next item's counted first wait
+    // still leaves exactly the 16 stores in flight.
+    float rs[2] = {0.0f, 0.0f};
+    f32x4_t rwv[2][2][4];
+    if (kEpi == kEpiStoreRouter) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) rs[i] = p.rdl[row0 + min(wm * 64 + i * 32 + r32, rows - 1)];
+      const float* rwg = p.rw + static_cast<int64_t>(group) * p.N + nt * WideCfg::BN + wn * 128;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            rwv[h][jj][rr] = *reinterpret_cast<const f32x4_t*>(rwg + h * 64 + jj * 32 + rr * 8 + g * 4);
+    }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -436,8 +456,12 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const f32x16_t& a = acc[i][2 * h + jj];
-            wide_park(region, r32, jj * 64 + rr * 16 + g * 8, a[4 * rr], a[4 * rr + 1],
-                      a[4 * rr + 2], a[4 * rr + 3]);
+            float v[4] = {a[4 * rr], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]};
+            if (kEpi == kEpiStoreRouter) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = __builtin_fmaf(rs[i], rwv[h][jj][rr][q], v[q]);
+            }
+            wide_park(region, r32, jj * 64 + rr * 16 + g * 8, v[0], v[1], v[2], v[3]);
           }
         const int col = nt * WideCfg::BN + wn * 128 + h * 64;
         wide_drain32(region, c + (orow + i * 32) * p.ldc + col, p.ldc, wrows - i * 32, lane);
@@ -586,9 +610,11 @@ void wide_gemm_kernel(const GemmArgs p, const int32_t* __restrict__ tiles,
     // The buffer of the last stage is free once every wave is done with it
     // (the other one is receiving the next item's first stage).
     wide_barrier();
-    wide_epilogue<kEpi>(p, acc, smem + (buf ^ 1) * kWideStage + wave * (kEpi == kEpiStore ? 4096 : 8192),
+    wide_epilogue<kEpi>(p, acc,
+                        smem + (buf ^ 1) * kWideStage +
+                            wave * ((kEpi == kEpiStore || kEpi == kEpiStoreRouter) ? 4096 : 8192),
                         kEpi == kEpiCombine ? smem + 2 * kWideStage + wave * 4096 : nullptr,
-                        cur.row0, cur.rows, nt, wm, wn, g, r32, lane);
+                        cur.row0, cur.rows, nt, wm, wn, g, r32, lane, cur.group);
     stores_out = wide_epilogue_stores<kEpi>(p);
 
     if (nxt.rows <= 0) break;
