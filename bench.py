@@ -81,8 +81,6 @@ def bwd_work(p):
     S = T * k
     es = 2 if p.dtype == "bf16" else 4
     w = {
-        # token rows and dl read, per-piece partials written
-        "bwd_router_partial": (2 * S * d, T * d * es + S * 8 + ((S + p.block_m - 1) // p.block_m + E) * d * 4),
         # dA|dB and gate/up weights read, per-slot dX written
         "bwd_gate_up_dgrad": (2 * S * 2 * h * d, S * 2 * h * es + E * 2 * h * d * es + S * d * es),
         # token rows and dA|dB read, fp32 dW_gate, dW_up written
@@ -91,7 +89,10 @@ def bwd_work(p):
         "bwd_dx": (2 * S * d, S * d * es + E * d * 4 + S * 8 + 2 * T * d * es),
     }
     if p.dtype == "bf16":
+        ks = max(1, min(64, T // 256))
         w.update({
+            # tokens and the dl hi/lo table read, the splits' fp32 partials written
+            "bwd_router_wgrad": (2 * T * d * 128, T * d * es + T * 128 * 2 + ks * d * 128 * 4),
             # grad_out rows (once), down weights, saved gate/up and the sorted
             # rows' combine weights read; dA|dB, w H and the dw parts written
             "bwd_down_dgrad": (2 * S * d * h, T * d * es + E * h * d * es + S * 2 * h * es + S * 4
@@ -103,6 +104,8 @@ def bwd_work(p):
         w.update({
             # grad_out and y read, dY written, weights / slot map read, dl written
             "bwd_combine": (2 * S * d, T * d * es + S * d * es + S * d * es + S * 12),
+            # token rows and dl read, per-piece partials written
+            "bwd_router_partial": (2 * S * d, T * d * es + S * 8 + ((S + p.block_m - 1) // p.block_m + E) * d * 4),
             # dY, down weights and saved gate/up read, dA|dB written
             "bwd_down_dgrad": (2 * S * d * h, S * d * es + E * h * d * es + 2 * S * 2 * h * es),
             # H and dY read, fp32 dW_down written
@@ -162,6 +165,10 @@ def trace_name(kernel):
     m = re.search(r"wgrad(?:_tr)?_kernel<.*>, (true|false), (true|false)>", kernel)
     if m:
         if m.group(1) == "true":
+            # dense: the router's split GEMM (128-row M tiles at its size) or
+            # the shared expert's weight gradients
+            if "TrCfg<128, 4>" in kernel:
+                return "bwd_router_wgrad"
             return "bwd_shared_wgrad_down"
         return "bwd_wgrad_gate_up" if m.group(2) == "true" else "bwd_wgrad_down"
     m = (re.search(r"wide_gemm_kernel<(true|false), (\d), (true|false)>", kernel) or

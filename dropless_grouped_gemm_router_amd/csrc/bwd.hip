@@ -293,15 +293,17 @@ __global__ __launch_bounds__(kRowThreads) void router_reduce_kernel(
 
 // bf16 path, before the down dgrad: the combine weight of each sorted
 // row's slot (ws[r] = w[perm[r]]), the zero row the weight-gradient loads
-// read past a group's end, and the router transposed for dx (wrT[e][j] =
-// wr[j][e], so that its columns are contiguous rows).
+// read past a group's end, the router transposed for dx (wrT[e][j] =
+// wr[j][e], so that its columns are contiguous rows), and the zeroed dl
+// table the router step fills (dlhl_n 16-byte pieces).
 __global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(
     int64_t rows, const int32_t* __restrict__ perm, const float* __restrict__ w,
     float* __restrict__ ws, float* __restrict__ zero_row, int zero_n, const float* __restrict__ wr,
-    int d, int E, float* __restrict__ wrT) {
+    int d, int E, float* __restrict__ wrT, u32x4* __restrict__ dlhl, int64_t dlhl_n) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kRowThreads;
   const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
   for (int64_t i = i0; i < zero_n; i += stride) zero_row[i] = 0.0f;
+  for (int64_t i = i0; i < dlhl_n; i += stride) dlhl[i] = u32x4{0u, 0u, 0u, 0u};
   const int64_t dE = static_cast<int64_t>(d) * E;
   for (int64_t i = i0; i < dE; i += stride) {
     const int64_t e = i / d, j = i % d;
@@ -317,12 +319,24 @@ __global__ __launch_bounds__(kRowThreads) void bwd_prep_kernel(
 // order (0 for a slot capacity routing dropped: its y is 0), then dl_i =
 // w_i (dw_i - sum_j w_j dw_j) with the sum taken in rank order. K = k <= 8
 // issues all of a token's loads of one kind before using them.
+// With dlhl, each slot's dl also goes into row t of the table [T][128]
+// (bf16) as hi = bf16(dl) at column e and lo = bf16(dl - hi) at column 64 + e
+// (e = its expert; a token's experts are distinct), for the router weight
+// gradient's GEMM: hi + lo carries dl to about 2^-16 relative.
+__device__ __forceinline__ void dl_hilo(bf16_t* row, int e, float v) {
+  const bf16_t hi = f32_to_bf16(v);
+  row[e] = hi;
+  row[64 + e] = f32_to_bf16(v - bf16_to_f32(hi));
+}
+
+constexpr int kDlThreads = 64;  // one wave per block: more blocks than CUs at 16384 tokens
+
 template <int K>
-__global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
+__global__ __launch_bounds__(kDlThreads) void router_dl_kernel(
     int64_t ntok, int k, int nparts, int64_t rows, const float* __restrict__ dwp,
     const float* __restrict__ w, const int32_t* __restrict__ inv_perm, float* __restrict__ dl,
-    float* __restrict__ dls) {
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x;
+    float* __restrict__ dls, const int32_t* __restrict__ topk_idx, bf16_t* __restrict__ dlhl) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kDlThreads + threadIdx.x;
   if (t >= ntok) return;
   if constexpr (K > 0) {
     int64_t r[K];
@@ -348,6 +362,7 @@ __global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
       const float v = wv[i] * (dw[i] - sum);
       dl[t * K + i] = v;
       if (r[i] >= 0) dls[r[i]] = v;
+      if (dlhl) dl_hilo(dlhl + t * 128, topk_idx[t * K + i], v);
     }
   } else {
     auto dw_of = [&](int i) {
@@ -364,7 +379,38 @@ __global__ __launch_bounds__(kRowThreads) void router_dl_kernel(
       dl[t * k + i] = v;
       const int64_t r = inv_perm[t * k + i];
       if (r >= 0) dls[r] = v;
+      if (dlhl) dl_hilo(dlhl + t * 128, topk_idx[t * k + i], v);
     }
+  }
+}
+
+// bf16 router weight gradient, stage 2: dW_r[j][e] = sum over the token
+// splits, in split order, of part[s][j][e] + part[s][j][64 + e] (the hi and
+// lo halves of the dl table multiplied out), eight splits loaded at a time.
+__global__ __launch_bounds__(kRowThreads) void router_reduce_hl_kernel(
+    const float* __restrict__ part, int splits, int d, int E, float* __restrict__ dwr) {
+  constexpr int kBatch = 8;
+  const int64_t n = static_cast<int64_t>(d) * E;
+  const int64_t sstride = static_cast<int64_t>(d) * 128;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kRowThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kRowThreads) {
+    const int64_t j = i / E;
+    const int e = static_cast<int>(i % E);
+    const float* p0 = part + j * 128 + e;
+    float acc = 0.0f;
+    int sp = 0;
+    for (; sp + kBatch <= splits; sp += kBatch) {
+      float hi[kBatch], lo[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        hi[u] = p0[(sp + u) * sstride];
+        lo[u] = p0[(sp + u) * sstride + 64];
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) acc += hi[u] + lo[u];
+    }
+    for (; sp < splits; ++sp) acc += p0[sp * sstride] + p0[sp * sstride + 64];
+    dwr[i] = acc;
   }
 }
 
@@ -558,9 +604,9 @@ struct BwdLayout {
   // dY holds dY [S][d] (fp32) or w H [S][h] (bf16); dwp the bf16 dw parts,
   // wsr the bf16 combine weights and dls its router-logit gradients by
   // sorted row
-  size_t dY, dl, dls, dwp, wsr, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero, tiles256,
-      total;
-  int ks_sd, ks_sgu;
+  size_t dY, dl, dls, dwp, wsr, dlhl, rph, dAB, dXs, rpart, dABs, dxs, part_sd, part_sgu, wrT, zero,
+      tiles256, total;
+  int ks_sd, ks_sgu, ks_r;
 };
 
 int split_count(int64_t rows, int tiles) {
@@ -587,6 +633,12 @@ BwdLayout bwd_layout(const moe_problem& p) {
   L.dwp = o;      o = align_up(o + ((h + 127) / 128) * S * 4, 256);
   L.wsr = o;      o = align_up(o + S * 4, 256);
   L.dls = o;      o = align_up(o + S * 4, 256);
+  // bf16 router weight gradient: the dl hi/lo table and the token splits'
+  // partials (splits of at least 256 tokens, at most 64)
+  const bool bf = p.dtype == MOE_BF16;
+  L.ks_r = static_cast<int>(T / 256 < 1 ? 1 : (T / 256 > 64 ? 64 : T / 256));
+  L.dlhl = o;     o = align_up(o + (bf ? T * 128 * 2 : 0), 256);
+  L.rph = o;      o = align_up(o + (bf ? static_cast<size_t>(L.ks_r) * d * 128 * 4 : 0), 256);
   L.dAB = o;      o = align_up(o + S * 2 * h * es, 256);
   L.dXs = o;      o = align_up(o + S * d * es, 256);
   L.rpart = o;    o = align_up(o + max_tiles * d * 4, 256);
@@ -744,6 +796,7 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
   // in bf16, the combine weights by sorted row for the down dgrad).
   const void* zero_row = W + L.zero;
   float* wsr = reinterpret_cast<float*>(W + L.wsr);
+  bf16_t* dlhl = std::is_same<T, bf16_t>::value ? reinterpret_cast<bf16_t*>(W + L.dlhl) : nullptr;
   float* dls = reinterpret_cast<float*>(W + L.dls);
   float* wrT = reinterpret_cast<float*>(W + L.wrT);
   bool router_folded = false;
@@ -753,7 +806,8 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
     MOE_LAUNCH("bwd_prep", bwd_prep_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kRowThreads),
                0, s, S, r.perm, r.topk_w, wsr, reinterpret_cast<float*>(W + L.zero),
                static_cast<int>(kTrZeroBytes / 4), w.w_router, d, E,
-               reinterpret_cast<float*>(W + L.wrT));
+               reinterpret_cast<float*>(W + L.wrT), reinterpret_cast<u32x4*>(W + L.dlhl),
+               T_ * 128 * 2 / 16);
   }
   const int64_t row_blocks = (T_ + kRowThreads / 64 - 1) / (kRowThreads / 64);
 
@@ -774,18 +828,18 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
       t256_built = true;
       float* dwp = reinterpret_cast<float*>(W + L.dwp);
       down_dgrad_fused(p, w, r, sab, grad_out, wsr, dY, dAB, dwp, t256, mt256, s);
-      const dim3 dl_grid(static_cast<unsigned>((T_ + kRowThreads - 1) / kRowThreads));
+      const dim3 dl_grid(static_cast<unsigned>((T_ + kDlThreads - 1) / kDlThreads));
 #define MOE_DL_K(KK)                                                                         \
   case KK:                                                                                   \
-    MOE_LAUNCH("bwd_router_dl", router_dl_kernel<KK>, dl_grid, dim3(kRowThreads), 0, s, T_, \
-               k, h / 128, S, dwp, r.topk_w, r.inv_perm, dl, dls);                                \
+    MOE_LAUNCH("bwd_router_dl", router_dl_kernel<KK>, dl_grid, dim3(kDlThreads), 0, s, T_,  \
+               k, h / 128, S, dwp, r.topk_w, r.inv_perm, dl, dls, r.topk_idx, dlhl);                                \
     break;
       switch (k) {
         MOE_DL_K(1) MOE_DL_K(2) MOE_DL_K(3) MOE_DL_K(4) MOE_DL_K(5) MOE_DL_K(6) MOE_DL_K(7)
         MOE_DL_K(8)
         default:
-          MOE_LAUNCH("bwd_router_dl", router_dl_kernel<0>, dl_grid, dim3(kRowThreads), 0, s, T_, k,
-                     h / 128, S, dwp, r.topk_w, r.inv_perm, dl, dls);
+          MOE_LAUNCH("bwd_router_dl", router_dl_kernel<0>, dl_grid, dim3(kDlThreads), 0, s, T_, k,
+                     h / 128, S, dwp, r.topk_w, r.inv_perm, dl, dls, r.topk_idx, dlhl);
       }
 #undef MOE_DL_K
     } else {
@@ -809,12 +863,37 @@ hipError_t bwd_t(const moe_problem& p, const void* x, const moe_weights& w, cons
       // a13: down dgrad from dY
       down_dgrad_dy<T>(p, w, r, sab, dY, dAB, s);
     }
-    // a12: router weight gradient (tile partials, then a per-expert ordered sum)
-    MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
-               dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
-               r.expert_offsets, E, p.block_m, rpart);
-    MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
-               r.expert_offsets, E, p.block_m, d, g.w_router);
+    // a12: router weight gradient
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      // dW_r = x^T DL as a GEMM over token splits: DL is the dl table
+      // (hi | lo halves, one row per token), then the splits and halves
+      // summed in a fixed order
+      WgradArgs a{};
+      a.a = x;
+      a.lda = d;
+      a.b = dlhl;
+      a.ldb = 128;
+      a.M = d;
+      a.N = 128;
+      a.rows_total = T_;
+      a.splits = L.ks_r;
+      a.c = reinterpret_cast<float*>(W + L.rph);
+      a.nsplit = 128;
+      a.ldc = 128;
+      a.c_group_stride = static_cast<int64_t>(d) * 128;
+      wgrad<T, false, true>("bwd_router_wgrad", a, L.ks_r, zero_row, s);
+      MOE_LAUNCH("bwd_router_reduce", router_reduce_hl_kernel,
+                 dim3(static_cast<unsigned>((static_cast<int64_t>(d) * E + kRowThreads - 1) / kRowThreads)),
+                 dim3(kRowThreads), 0, s,
+                 reinterpret_cast<const float*>(W + L.rph), L.ks_r, d, E, g.w_router);
+    } else {
+      // tile partials, then a per-expert ordered sum
+      MOE_LAUNCH("bwd_router_partial", router_partial_kernel<T>, dim3(static_cast<unsigned>(max_tiles)),
+                 dim3(kRowThreads), 0, s, static_cast<const T*>(x), d, k, r.perm, dl,
+                 r.expert_offsets, E, p.block_m, rpart);
+      MOE_LAUNCH("bwd_router_reduce", router_reduce_kernel, dim3(E), dim3(kRowThreads), 0, s, rpart,
+                 r.expert_offsets, E, p.block_m, d, g.w_router);
+    }
     // a15: gate/up dgrad (bf16: with the router term of each kept slot)
     router_folded = gate_up_dgrad<T>(p, w, r, dAB, dXs, t256, t256_built, t256_built ? dls : nullptr,
                                      t256_built ? wrT : nullptr, s);
