@@ -214,7 +214,8 @@ MOE_EXPORT int moe_bwd(const moe_problem* p, const void* x, const moe_weights* w
   if (!w || !r || !ok_ptr(x) || !ok_ptr(w->w_router, 4) || !ok_ptr(w->w_gate) || !ok_ptr(w->w_up) ||
       !ok_ptr(w->w_down) || !ok_ptr(r->topk_idx, 4) || !ok_ptr(r->topk_w, 4) ||
       !ok_ptr(r->expert_offsets, 4) || !ok_ptr(r->perm, 4) || !ok_ptr(r->inv_perm, 4) ||
-      !ok_ptr(r->tiles, 4) || !ok_ptr(r->num_tiles, 4) || !ok_ptr(y_sorted) ||
+      !ok_ptr(r->tiles, 4) || !ok_ptr(r->num_tiles, 4) ||
+      (p->dtype != MOE_BF16 && !ok_ptr(y_sorted)) ||  // the bf16 backward does not read it
       !ok_ptr(saved, 256) || !ok_ptr(grad_out) || !ok_ptr(grad_x) || !ok_ptr(g->w_gate) ||
       !ok_ptr(g->w_up) || !ok_ptr(g->w_down) || !ok_ptr(workspace, 256))
     return MOE_ERR_INVALID;

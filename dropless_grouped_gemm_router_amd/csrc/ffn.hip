@@ -347,7 +347,8 @@ void ffn_routed_t(const moe_problem& p, const void* x, const moe_weights& w,
   char* SV = static_cast<char*>(saved);
   const int h = p.d_hidden;
   if (!packed) pack_weights_t<T>(p, w, ws, saved != nullptr, false, s);
-  T* hbuf = saved ? reinterpret_cast<T*>(SV + L.sv_h) : reinterpret_cast<T*>(W + L.h_sorted);
+  T* hbuf = (saved && !std::is_same<T, bf16_t>::value) ? reinterpret_cast<T*>(SV + L.sv_h)
+                                                        : reinterpret_cast<T*>(W + L.h_sorted);
   T* sa = saved ? reinterpret_cast<T*>(SV + L.sv_ab) : nullptr;
   T* sb = saved ? sa + h : nullptr;
   routed_ffn<T>(p, x, r, W + L.gu_packed, W + L.down_packed, hbuf, y_sorted, sa, sb, x_sorted,
@@ -397,13 +398,16 @@ FfnLayout ffn_layout(const moe_problem& p, bool training) {
   L.down_packed = o;  o = align_up(o + E * d * h * es, 256);
   L.sgu_packed = o;   o = align_up(o + 2 * hs * d * es, 256);
   L.sdown_packed = o; o = align_up(o + d * hs * es, 256);
-  L.h_sorted = o;     o = align_up(o + (training ? 0 : S * h * es), 256);
+  // The routed H stays in the workspace unless the fp32 backward needs it
+  // saved (the bf16 backward recomputes it from the saved pre-activations).
+  const bool save_h = training && p.dtype != MOE_BF16;
+  L.h_sorted = o;     o = align_up(o + (save_h ? 0 : S * h * es), 256);
   L.h_shared = o;     o = align_up(o + (training ? 0 : T * hs * es), 256);
   L.tiles256 = o;     o = align_up(o + retile_bytes(static_cast<int64_t>(S), p.experts), 256);
   L.total = o;
   size_t v = 0;
   L.sv_ab = v;  v = align_up(v + S * 2 * h * es, 256);
-  L.sv_h = v;   v = align_up(v + S * h * es, 256);
+  L.sv_h = v;   v = align_up(v + (p.dtype == MOE_BF16 ? 0 : S * h * es), 256);
   L.sv_sab = v; v = align_up(v + T * 2 * hs * es, 256);
   L.sv_sh = v;  v = align_up(v + T * hs * es, 256);
   L.sv_total = v;

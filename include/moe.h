@@ -186,8 +186,9 @@ size_t moe_workspace_bytes(const moe_problem* p, int training);
 
 /*
  * Bytes of the activation buffer that moe_ffn_fwd fills for moe_bwd
- * (host): gate and up pre-activations and the gated hidden values of every
- * token-slot, and the same for the shared expert; all in dtype.
+ * (host): gate and up pre-activations of every token-slot (and, in fp32,
+ * their gated hidden values; the bf16 backward recomputes those), and the
+ * shared expert's pre-activations and hidden values; all in dtype.
  */
 size_t moe_saved_bytes(const moe_problem* p);
 
@@ -316,8 +317,10 @@ int moe_forward(const moe_problem* p, int dispatch, const void* x, const moe_wei
  * through the renormalised weights:
  *   dy = w * G, dw = <G, y>, dl = w (dw - sum w dw) on the kept experts,
  *   and the chain rule through both expert projections and SiLU.
- * Reads x, the weights, the routing state, y_sorted and saved from the
- * forward, and grad_out [tokens, d_model] (dtype). Writes grad_x
+ * Reads x, the weights, the routing state, saved and (fp32 only) y_sorted
+ * from the forward, and grad_out [tokens, d_model] (dtype); in bf16 dw is
+ * evaluated as <G W_down^T, H>, which equals <G, y>, so y_sorted is not
+ * read and may be NULL. Writes grad_x
  * [tokens, d_model] (dtype) and every array of g (fp32; the shared ones
  * only when d_shared > 0). workspace: >= moe_workspace_bytes(p, 1).
  * saved must be the moe_saved_bytes(p) buffer moe_ffn_fwd filled.

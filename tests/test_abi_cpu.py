@@ -244,6 +244,13 @@ def test_bwd_argument_errors():
     assert need > B.moe_workspace_bytes(P, training=False)
     expect(B.MOE_ERR_WORKSPACE, B.moe_bwd, P, x, w, r, a[0], a[1], a[2], a[3], g, ws,
            workspace_bytes=need - 1, stream=0)
+    # y_sorted: required in fp32, not read (may be NULL) in bf16
+    p32 = Problem(100, 8, 2, 256, 128, 128, "fp32", 64)
+    need32 = B.moe_workspace_bytes(p32, training=True)
+    expect(B.MOE_ERR_INVALID, B.moe_bwd, p32, x, w, r, None, a[1], a[2], a[3], g, ws,
+           workspace_bytes=need32, stream=0)
+    expect(B.MOE_ERR_WORKSPACE, B.moe_bwd, P, x, w, r, None, a[1], a[2], a[3], g, ws,
+           workspace_bytes=need - 1, stream=0)
     # the backward tiles hidden widths by 128
     p64 = Problem(100, 8, 2, 256, 192, 128, "bf16", 64)
     expect(B.MOE_ERR_UNSUPPORTED, B.moe_bwd, p64, x, w, r, a[0], a[1], a[2], a[3], g, ws,
