@@ -475,8 +475,35 @@ hipError_t launch_forward(const moe_problem& p, int dispatch, const void* x, con
   void* x_sorted = dispatch == MOE_DISPATCH_SORTED ? W + L.x_sorted : nullptr;
   const bool bf = p.dtype == MOE_BF16;
   // Unfused, the shared expert depends on nothing but the tokens and its
-  // weights: with a second stream it runs there beside route, permute and
-  // the routed FFN, and the combine waits for it.
+  // weights: with a second stream it runs there beside the routed path, and
+  // the combine waits for it. From 65536 tokens on it starts after the
+  // permutation: beside route and permute its persistent GEMMs hold the CUs
+  // the small permute kernels need (count and scan stretched to tens of
+  // times their own duration), and forward steps at 131072 tokens measured
+  // 1.45 -> 1.42 ms; at 16384 tokens the early start overlaps more of the
+  // shared expert and is the faster one (train step 0.78 vs 0.79 ms).
+  if (p.d_shared > 0 && !L.fused && side != nullptr && side != s && p.tokens >= 65536) {
+    if (bf) pack_weights_t<bf16_t>(p, w, ws, saved != nullptr, true, s);
+    else pack_weights_t<float>(p, w, ws, saved != nullptr, true, s);
+    hipError_t e = launch_route(p.dtype, x, w.w_router, p.tokens, p.d_model, p.experts, p.top_k,
+                                r.topk_idx, r.topk_w, s);
+    if (e != hipSuccess) return e;
+    e = launch_permute(p.tokens, p.top_k, p.experts, p.block_m, p.capacity, r.topk_idx,
+                       r.expert_offsets, r.perm, r.inv_perm, r.tiles, r.num_tiles, W + L.permute, s);
+    if (e != hipSuccess) return e;
+    StreamFork fork(s, side);
+    e = fork.fork();
+    if (e != hipSuccess) return e;
+    if (bf) ffn_shared_t<bf16_t>(p, x, w, shared_out, saved, ws, nullptr, fork.side(), true);
+    else ffn_shared_t<float>(p, x, w, shared_out, saved, ws, nullptr, fork.side(), true);
+    if (bf) ffn_routed_t<bf16_t>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, true);
+    else ffn_routed_t<float>(p, x, w, r, y_sorted, saved, ws, x_sorted, s, true);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = fork.join();
+    if (e != hipSuccess) return e;
+    return launch_combine(p.dtype, p.tokens, p.top_k, p.d_model, y_sorted, r.topk_w, r.inv_perm,
+                          shared_out, out, s);
+  }
   if (p.d_shared > 0 && !L.fused && side != nullptr && side != s) {
     // The routed weights are packed first on the side stream too, beside the
     // router kernel (which leaves room on every CU for the pack kernel's

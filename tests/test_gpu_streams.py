@@ -91,6 +91,35 @@ def test_back_to_back_forwards_use_their_own_weights():
         assert bits_equal(refs[i % 2], o), f"call {i}"
 
 
+def test_late_fork_gives_one_stream_bits():
+    """From 65536 tokens on, moe_forward packs and permutes on the caller's
+    stream and forks the shared expert only then. Two weight sets
+    alternating on one workspace (forward and train step) must give the
+    bits of one-stream calls."""
+    import torch
+    p = Problem(65536, 16, 2, 256, 128, 256, "bf16", 256)
+    cases = [Case(p, seed=41, training=True), Case(p, seed=42, training=True)]
+    refs = []
+    for c in cases:
+        buf = B.allocate(p, training=True, dispatch="gather")
+        B.forward_dispatch(p, "gather", c.dev["x"], c.weights(), buf, training=True)
+        B.backward(p, c.dev["x"], c.weights(), c.dev["grad_out"], buf)
+        torch.cuda.synchronize()
+        refs.append([buf.out.clone(), buf.grad_x.clone()] + [t.clone() for t in buf.grads.values()])
+    assert not bits_equal(refs[0][0], refs[1][0])
+    buf = B.allocate(p, training=True, dispatch="gather")
+    side = torch.cuda.Stream()
+    for i in range(4):
+        c = cases[i % 2]
+        B.forward_dispatch(p, "gather", c.dev["x"], c.weights(), buf, training=True,
+                           side_stream=side)
+        B.backward(p, c.dev["x"], c.weights(), c.dev["grad_out"], buf, side_stream=side)
+        got = [buf.out.clone(), buf.grad_x.clone()] + [t.clone() for t in buf.grads.values()]
+        torch.cuda.synchronize()
+        for j, (a, b) in enumerate(zip(refs[i % 2], got)):
+            assert bits_equal(a, b), f"call {i}, output {j}"
+
+
 def test_train_step_replays_from_a_hip_graph():
     """Forward (with saved activations) and backward captured once, replayed
     on new token values; every replay equals the eager step bit for bit."""
