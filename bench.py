@@ -148,8 +148,10 @@ def trace_name(kernel):
     if "route_kernel" in kernel or "route_resident_kernel" in kernel:
         return "route"
     for k, name in (("combine_bwd", "bwd_combine"), ("router_partial", "bwd_router_partial"),
-                    ("router_reduce", "bwd_router_reduce"), ("router_transpose", "bwd_router_transpose"),
+                    ("router_reduce", "bwd_router_reduce"), ("router_reduce_hl", "bwd_router_reduce"),
+                    ("router_transpose", "bwd_router_transpose"), ("router_dl", "bwd_router_dl"),
                     ("split_reduce", "bwd_split_reduce"), ("dx_gather", "bwd_dx"),
+                    ("down_dgrad", "bwd_down_dgrad"), ("bwd_prep", "bwd_prep"),
                     ("fill_zero", "fill_zero"), ("retile", "retile")):
         if f"{k}_kernel" in kernel or f"{k}_k_kernel" in kernel:
             return name
@@ -162,15 +164,19 @@ def trace_name(kernel):
         return "pack_weights"
     if "sort_rows_kernel" in kernel:
         return "sort_rows"
-    m = re.search(r"wgrad(?:_tr)?_kernel<.*>, (true|false), (true|false)>", kernel)
+    m = re.search(r"wgrad_tr_kernel<moe::TrCfg<(\d+), \d+>, (true|false), (true|false)>", kernel)
     if m:
-        if m.group(1) == "true":
+        if m.group(2) == "true":
             # dense: the router's split GEMM (128-row M tiles at its size) or
-            # the shared expert's weight gradients
-            if "TrCfg<128, 4>" in kernel:
-                return "bwd_router_wgrad"
+            # the shared expert's two weight gradients (down first)
+            return "bwd_router_wgrad" if m.group(1) == "128" else "bwd_shared_wgrad_down"
+        # the routed weight gradients, down first
+        return "bwd_wgrad_down"
+    m = re.search(r"wgrad_kernel<[^,]*, (true|false), (true|false)>", kernel)
+    if m:  # fp32: <T, gathered A, dense>
+        if m.group(2) == "true":
             return "bwd_shared_wgrad_down"
-        return "bwd_wgrad_gate_up" if m.group(2) == "true" else "bwd_wgrad_down"
+        return "bwd_wgrad_gate_up" if m.group(1) == "true" else "bwd_wgrad_down"
     m = (re.search(r"wide_gemm_kernel<(true|false), (\d), (true|false)>", kernel) or
          re.search(r"gemm_kernel<.*>, (true|false), (\d), (true|false)>", kernel))
     if m:
@@ -187,7 +193,7 @@ def trace_name(kernel):
 # within one step is the n-th stage named here.
 _SECOND_USE = {"shared_down": "bwd_shared_gate_up_dgrad", "gemm_down": "bwd_gate_up_dgrad",
                "bwd_shared_wgrad_down": "bwd_shared_wgrad_gate_up", "retile": "bwd_retile",
-               "bwd_split_reduce": "bwd_split_reduce_gate_up"}
+               "bwd_split_reduce": "bwd_split_reduce_gate_up", "bwd_wgrad_down": "bwd_wgrad_gate_up"}
 
 
 def step_trace_names(kernels):
