@@ -276,7 +276,10 @@ def load_traffic(path, workload_name):
 STAGE_PROBE_MODES = {0: "no loads (operands stay in LDS)", 1: "token half loaded (32 KiB)",
                      2: "weight half loaded (32 KiB)", 3: "whole stage loaded (64 KiB)",
                      4: "64 KiB into registers", 5: "64 KiB of LDS stores, no loads",
-                     6: "64 KiB issued by waves 0-3 only"}
+                     6: "64 KiB issued by waves 0-3 only",
+                     7: "MFMA only (fragments held in registers)",
+                     8: "whole stage, four waves of 128x128",
+                     9: "whole stage, token rows three-deep"}
 
 
 def stage_probe(reps=20):
@@ -290,20 +293,28 @@ def stage_probe(reps=20):
     torch.cuda.set_device(0)
     lib = ctypes.CDLL(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "libmoe_probe.so"))
     lib.moe_stage_probe.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                    ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_float)]
     grid, items = 256, 16
     flops = 2.0 * 256 * 256 * 512 * grid * items
     regions = [(4096, 0, "4 MiB of token rows in order (L2)"),
                (131072, 1, "rows hashed over 128 MiB (Infinity Cache)"),
                (1 << 20, 1, "rows hashed over 1 GiB (HBM)")]
-    runs = [(m, regions[0]) for m in range(7)] + [(3, regions[1]), (3, regions[2])]
-    for mode, (rows, rnd, where) in runs:
+    # zero operands (every mode), then random bf16 operands for the modes
+    # that bound a real GEMM: the MFMA pipes alone, the LDS-fed loop, and
+    # the whole stage from each place the token rows can come from
+    runs = ([(m, regions[0], 0) for m in range(8)] +
+            [(m, r, 0) for r in regions[1:] for m in (3, 8, 9)] +
+            [(7, regions[0], 1), (0, regions[0], 1), (3, regions[0], 1), (3, regions[1], 1),
+             (3, regions[2], 1), (8, regions[1], 1), (9, regions[1], 1), (9, regions[2], 1)])
+    for mode, (rows, rnd, where), data in runs:
         ms = ctypes.c_float(0.0)
-        rc = lib.moe_stage_probe(mode, rows, rnd, grid, items, reps, ctypes.byref(ms))
+        rc = lib.moe_stage_probe(mode, rows, rnd, data, grid, items, reps, ctypes.byref(ms))
         if rc != 0:
             raise RuntimeError(f"moe_stage_probe(mode {mode}) returned {rc}")
         tf = flops / (ms.value * 1e-3) / 1e12
         print(json.dumps({"stage_probe": STAGE_PROBE_MODES[mode], "mode": mode, "tokens": where,
+                          "data": "random bf16" if data else "zeros",
                           "ms": round(ms.value, 4), "TFLOP/s": round(tf, 1),
                           "frac_mfma_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}), flush=True)
 

@@ -39,13 +39,14 @@ def test_stage_probe_library_loads():
     lib = ctypes.CDLL(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "libmoe_probe.so"))
     fn = lib.moe_stage_probe
     fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                   ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+                   ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
     ms = ctypes.c_float(0.0)
-    assert fn(7, 4096, 0, 256, 16, 1, ctypes.byref(ms)) == -1      # no such mode
-    assert fn(3, 100, 0, 256, 16, 1, ctypes.byref(ms)) == -1       # region under one tile
-    assert fn(3, (1 << 20) + 1, 0, 256, 16, 1, ctypes.byref(ms)) == -1
-    assert fn(3, 4096, 0, 0, 16, 1, ctypes.byref(ms)) == -1
-    assert fn(3, 4096, 0, 256, 16, 1, None) == -1
+    assert fn(10, 4096, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1     # no such mode
+    assert fn(3, 100, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1       # region under one tile
+    assert fn(3, (1 << 20) + 1, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1
+    assert fn(3, 4096, 0, 2, 256, 16, 1, ctypes.byref(ms)) == -1      # no such data kind
+    assert fn(3, 4096, 0, 0, 0, 16, 1, ctypes.byref(ms)) == -1
+    assert fn(3, 4096, 0, 0, 256, 16, 1, None) == -1
 
 
 def test_param_count_and_tiles():
