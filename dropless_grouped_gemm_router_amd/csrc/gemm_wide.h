@@ -169,6 +169,19 @@ __device__ __forceinline__ void wide_park(char* region, int row, int byte, float
   asm volatile("ds_write_b64 %0, %1" : : "v"(lds_addr(region + row * 128 + pos)), "v"(d) : "memory");
 }
 
+// A 16-byte row piece, as a nontemporal store when kNT. The SwiGLU outputs
+// (H, and the pre-activations a training forward saves) are written that
+// way: they are read back only by later kernels, and kept out of L2 they
+// leave it to the token rows and weights the GEMM re-reads (forward at
+// 131072 tokens, E=64, top-8: 1.376 -> 1.354 ms median, same bits). The
+// plain-store epilogues measured the same or slower with it (the routed
+// down GEMM's y_sorted stores 0.251 -> 0.267 ms).
+template <bool kNT>
+__device__ __forceinline__ void wide_store16(bf16_t* dst, const u32x4& v) {
+  if (kNT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+  else *reinterpret_cast<u32x4*>(dst) = v;
+}
+
 // Writes the parked block: region row r goes to dst + r * ld (elements),
 // 64 bf16 columns, for rows r < rows; rows may be 0 or negative (a wave
 // block past the tile's end), with dst + (rows - 1) * ld then the tile's
@@ -177,6 +190,7 @@ __device__ __forceinline__ void wide_park(char* region, int row, int byte, float
 // values are that row's, bit for bit, and it is written over that row.
 // The fixed store count lets the next item's first wait leave these
 // stores in flight (wide_wait_stores).
+template <bool kNT>
 __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int64_t ld, int rows,
                                            int lane) {
   // All eight LDS reads first (always in bounds), then the stores.
@@ -206,7 +220,7 @@ __device__ __forceinline__ void wide_drain(const char* region, bf16_t* dst, int6
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int r = k * 8 + (lane >> 3);
-    *reinterpret_cast<u32x4*>(dst + min(r, rows - 1) * ld + c * 8) = v[k];
+    wide_store16<kNT>(dst + min(r, rows - 1) * ld + c * 8, v[k]);
   }
 }
 
@@ -234,7 +248,7 @@ __device__ __forceinline__ void wide_drain32(const char* region, bf16_t* dst, in
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int r = k * 8 + (lane >> 3);
-    *reinterpret_cast<u32x4*>(dst + min(r, rows - 1) * ld + c * 8) = v[k];
+    wide_store16<false>(dst + min(r, rows - 1) * ld + c * 8, v[k]);
   }
 }
 
@@ -469,12 +483,12 @@ __device__ __forceinline__ void wide_epilogue(const GemmArgs& p,
   } else {
     const int hcol = nt * (WideCfg::BN / 2) + wn * 64;
     wide_park_swiglu<0>(acc, region, g, r32);
-    wide_drain(region, c + orow * p.ldc + hcol, p.ldc, wrows, lane);
+    wide_drain<true>(region, c + orow * p.ldc + hcol, p.ldc, wrows, lane);
     if (p.sa) {
       wide_park_swiglu<1>(acc, region, g, r32);
-      wide_drain(region, static_cast<bf16_t*>(p.sa) + orow * p.lds + hcol, p.lds, wrows, lane);
+      wide_drain<true>(region, static_cast<bf16_t*>(p.sa) + orow * p.lds + hcol, p.lds, wrows, lane);
       wide_park_swiglu<2>(acc, region, g, r32);
-      wide_drain(region, static_cast<bf16_t*>(p.sb) + orow * p.lds + hcol, p.lds, wrows, lane);
+      wide_drain<true>(region, static_cast<bf16_t*>(p.sb) + orow * p.lds + hcol, p.lds, wrows, lane);
     }
   }
 }
