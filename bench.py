@@ -29,15 +29,44 @@ PEAK_VALU_TFLOPS = 78.6
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 TRAFFIC_TRAIN_FILE = os.path.join(ROOT, "profiles", "traffic_train.json")
-KERNEL_SOURCES = ["gemm_core.h", "gemm_wide.h", "gemm_launch.h", "ffn.hip", "route.hip",
-                  "permute.hip", "combine.hip", "common.h", "sort_rows.h", "bwd.hip", "gemm_wgrad.h"]
+KERNEL_SOURCES = ["gemm_core.h", "gemm_wide.h", "gemm_launch.h", "gemm_dgrad.h", "gemm_wgrad.h",
+                  "ffn.hip", "route.hip", "permute.hip", "combine.hip", "bwd.hip", "common.h",
+                  "sort_rows.h"]
+
+
+def strip_comments(src):
+    """C++ source without its comments and blank lines (string and character
+    literals kept), so that a comment edit does not mark the counters of an
+    unchanged kernel as stale."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = [ln.rstrip() for ln in "".join(out).split("\n")]
+    return "\n".join(ln for ln in lines if ln.strip())
 
 
 def kernel_source_hash():
+    """Hash of the kernel sources (comments stripped) that the stored
+    FETCH/WRITE counters were taken with."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "csrc", f)) as fh:
+            h.update(strip_comments(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

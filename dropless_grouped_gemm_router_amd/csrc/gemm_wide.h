@@ -172,8 +172,10 @@ __device__ __forceinline__ void wide_park(char* region, int row, int byte, float
 // A 16-byte row piece, as a nontemporal store when kNT. The SwiGLU outputs
 // (H, and the pre-activations a training forward saves) are written that
 // way: they are read back only by later kernels, and kept out of L2 they
-// leave it to the token rows and weights the GEMM re-reads (forward at
-// 131072 tokens, E=64, top-8: 1.376 -> 1.354 ms median, same bits). The
+// leave it to the token rows and weights the GEMM re-reads (the shared
+// gate/up GEMM at 131072 tokens reads 1.06x its algorithmic bytes past L2
+// instead of 1.63x; forward at 131072 tokens, E=64, top-8: 1.376 -> 1.354
+// ms median, same bits). The
 // plain-store epilogues measured the same or slower with it (the routed
 // down GEMM's y_sorted stores 0.251 -> 0.267 ms).
 template <bool kNT>
