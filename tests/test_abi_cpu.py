@@ -304,3 +304,17 @@ def test_training_workspace_for_narrow_shared_width():
     it, but sizing the training forward's workspace must still work."""
     p = Problem(77, 5, 3, 128, 128, 64, "bf16", 32)
     assert B.moe_workspace_bytes(p, True) >= B.moe_workspace_bytes(p, False) > 0
+
+
+def test_kernel_source_hash_ignores_comments_only():
+    """The stored FETCH/WRITE counters stay valid across comment edits and go
+    stale on any code change: the hash strips comments (not string or
+    character literals that hold comment markers) and blank lines."""
+    import bench
+    a = 'int a = 1;  // note\n/* block\n comment */ const char* s = "//x/*y*/";\n\nchar c = \'/\';\n'
+    b = 'int a = 1;\nconst char* s = "//x/*y*/";\nchar c = \'/\';   // other note\n'
+    assert bench.strip_comments(a) == 'int a = 1;\n const char* s = "//x/*y*/";\nchar c = \'/\';'
+    assert bench.strip_comments(b) == 'int a = 1;\nconst char* s = "//x/*y*/";\nchar c = \'/\';'
+    assert bench.strip_comments("x = 2; // y\n") != bench.strip_comments("x = 3; // y\n")
+    assert "gemm_dgrad.h" in bench.KERNEL_SOURCES
+    assert len(bench.kernel_source_hash()) == 16
