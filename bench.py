@@ -308,7 +308,8 @@ STAGE_PROBE_MODES = {0: "no loads (operands stay in LDS)", 1: "token half loaded
                      6: "64 KiB issued by waves 0-3 only",
                      7: "MFMA only (fragments held in registers)",
                      8: "whole stage, four waves of 128x128",
-                     9: "whole stage, token rows three-deep"}
+                     9: "whole stage, token rows three-deep",
+                     10: "whole stage, four waves, loads spread between MFMAs"}
 
 
 def stage_probe(reps=20):
@@ -333,9 +334,10 @@ def stage_probe(reps=20):
     # that bound a real GEMM: the MFMA pipes alone, the LDS-fed loop, and
     # the whole stage from each place the token rows can come from
     runs = ([(m, regions[0], 0) for m in range(8)] +
-            [(m, r, 0) for r in regions[1:] for m in (3, 8, 9)] +
+            [(m, r, 0) for r in regions[1:] for m in (3, 8, 9, 10)] +
             [(7, regions[0], 1), (0, regions[0], 1), (3, regions[0], 1), (3, regions[1], 1),
-             (3, regions[2], 1), (8, regions[1], 1), (9, regions[1], 1), (9, regions[2], 1)])
+             (3, regions[2], 1), (8, regions[1], 1), (9, regions[1], 1), (9, regions[2], 1),
+             (10, regions[1], 1), (10, regions[2], 1)])
     for mode, (rows, rnd, where), data in runs:
         ms = ctypes.c_float(0.0)
         rc = lib.moe_stage_probe(mode, rows, rnd, data, grid, items, reps, ctypes.byref(ms))

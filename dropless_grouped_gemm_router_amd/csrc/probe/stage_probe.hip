@@ -17,6 +17,8 @@
 //      threads) instead of eight of 64 x 128
 //   9  as 3 with the token half in a ring of three 32 KiB buffers, issued
 //      two stages ahead, and the weight half in two (160 KiB of LDS)
+//  10  as 8 with the next stage's loads and the next K step's fragment
+//      reads spread between the MFMAs by scheduling barriers
 // Token rows come from a region of `a_rows` 1 KiB rows, read in order or
 // (random != 0) at hashed rows, as gathered expert rows are; weights from a
 // 2 MiB region (8 groups of 256 rows x 512 bf16), L2-resident. K = 512.
@@ -132,6 +134,11 @@ void stage_probe_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__
       for (int q = 0; q < 16; ++q) sum += acc[i][j][q];
   // a test that is practically never true; keeps the work alive
   if (sum == 1234.5f || sink == 0x12345678u) out[blockIdx.x * 512 + tid] = sum;
+}
+
+// Weight rows of item `item`: group item % 8 of the 2 MiB weight region.
+__device__ __forceinline__ const char* Bw_base(const bf16_t* Bw, int64_t item) {
+  return reinterpret_cast<const char*>(Bw) + (item % 8) * 256 * 1024;
 }
 
 // Modes 8 and 9: NW waves of WM x WN MFMA tiles each; RING 0 keeps the
@@ -261,6 +268,106 @@ void stage_token_ring_kernel(const bf16_t* A, const bf16_t* Bw, int64_t a_rows, 
   stage_ring<8, 2, 4, 1>(A, Bw, a_rows, random, items, out);
 }
 
+// Mode 10: four waves of 128 x 128 blocks, two 64 KiB stage buffers. Each K
+// step reads the next step's fragments and issues a quarter of the next
+// stage's 16 loads per wave, and scheduling barriers place them between
+// its 16 MFMAs ([MFMA][read][MFMA][read][MFMA][load][MFMA] four times).
+// The loads run unconditionally: past the last stage they fetch in-bounds
+// rows of a tile past this workgroup's share into the buffer nobody reads.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void stage_four_wave_spread_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Bw,
+                                   int64_t a_rows, int random, int items, float* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(1024))) char dyn[];
+  constexpr int kHalf = 8;  // loads per wave per half stage
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, r32 = lane & 31;
+  const int wm = wave / 2, wn = wave % 2;
+  const int a_frag = (wm * 128 + r32) * kWideRowBytes;
+  const int b_frag = 32768 + (wn * 128 + r32) * kWideRowBytes;
+  const int xr = lane >> 4;
+  const int chunk_off[2] = {((lane & 7) ^ xr) * 16, ((lane & 7) ^ (xr + 4)) * 16};
+  f32x16_t acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  const int total = items * 8;
+  const char* a_row[kHalf];
+  const char* b_base = Bw_base(Bw, 0);
+  auto rows_for = [&](int s) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * items + s / 8;
+#pragma unroll
+    for (int i = 0; i < kHalf; ++i) {
+      int64_t row = item * 256 + (wave * kHalf + i) * 8 + (lane >> 3);
+      if (random) row *= 2654435761ll;
+      row %= a_rows;
+      a_row[i] = reinterpret_cast<const char*>(A) + row * 1024 + chunk_off[i & 1];
+    }
+    b_base = Bw_base(Bw, item);
+  };
+  auto load1 = [&](int s, int u) {  // load u (0..15) of stage s
+    char* dst = dyn + (s & 1) * 65536;
+    const int koff = (s & 7) * 128;
+    if (u < kHalf) {
+      __builtin_amdgcn_global_load_lds(a_row[u] + koff, dst + (wave * kHalf + u) * 1024, 16, 0, 0);
+    } else {
+      const int i = u - kHalf;
+      const int r = (wave * kHalf + i) * 8 + (lane >> 3);
+      __builtin_amdgcn_global_load_lds(b_base + r * 1024 + chunk_off[i & 1] + koff,
+                                       dst + 32768 + (wave * kHalf + i) * 1024, 16, 0, 0);
+    }
+  };
+  rows_for(0);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) load1(0, u);
+  int sb = g ^ ((r32 >> 1) & 7);
+  for (int s = 0; s < total; ++s) {
+    wide_wait_all();
+    wide_barrier();
+    if (((s + 1) & 7) == 0) rows_for(s + 1);
+    const char* buf = dyn + (s & 1) * 65536;
+    asm volatile("" : "+v"(sb));
+    u32x4 xf[2][4], wf[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xf[0][i] = *reinterpret_cast<const u32x4*>(buf + a_frag + i * 4096 + (sb << 4));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wf[0][j] = *reinterpret_cast<const u32x4*>(buf + b_frag + j * 4096 + (sb << 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = q & 1, n = c ^ 1;
+      if (q < 3) {
+        const int sw = ((2 * (q + 1)) ^ sb) << 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xf[n][i] = *reinterpret_cast<const u32x4*>(buf + a_frag + i * 4096 + sw);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wf[n][j] = *reinterpret_cast<const u32x4*>(buf + b_frag + j * 4096 + sw);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load1(s + 1, q * 4 + u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Mfma<bf16_t>::step(wf[c][j], xf[c][i], acc[i][j]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wide_wait_all();
+  float sum = 0.0f;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int q = 0; q < 16; ++q) sum += acc[i][j][q];
+  if (sum == 1234.5f) out[blockIdx.x * 512 + tid] = sum;
+}
+
 #define PROBE_EXPORT extern "C" __attribute__((visibility("default")))
 
 // Hashed bf16 values, two per 32-bit word: random sign, exponent 2^-1 or
@@ -288,7 +395,7 @@ __global__ void probe_fill_kernel(uint32_t* p, int64_t n, int data) {
 // its own buffers (1 GiB of token rows at most). Returns 0 or a HIP error.
 PROBE_EXPORT int moe_stage_probe(int mode, int64_t a_rows, int random, int data, int grid,
                                  int items, int reps, float* ms) {
-  if (mode < 0 || mode > 9 || a_rows < 256 || a_rows > (int64_t{1} << 20) || data < 0 ||
+  if (mode < 0 || mode > 10 || a_rows < 256 || a_rows > (int64_t{1} << 20) || data < 0 ||
       data > 1 || grid < 1 || items < 1 || reps < 1 || !ms)
     return -1;
   bf16_t *A = nullptr, *Bw = nullptr;
@@ -310,10 +417,16 @@ PROBE_EXPORT int moe_stage_probe(int mode, int64_t a_rows, int random, int data,
   if (e == hipSuccess && mode == 8)
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(stage_four_wave_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
+  if (e == hipSuccess && mode == 10)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(stage_four_wave_spread_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 131072);
   auto launch = [&]() {
     if (mode == 8)
       hipLaunchKernelGGL(stage_four_wave_kernel, dim3(grid), dim3(256), 131072, 0, A, Bw, a_rows,
                          random, items, out);
+    else if (mode == 10)
+      hipLaunchKernelGGL(stage_four_wave_spread_kernel, dim3(grid), dim3(256), 131072, 0, A, Bw,
+                         a_rows, random, items, out);
     else if (mode == 9)
       hipLaunchKernelGGL(stage_token_ring_kernel, dim3(grid), dim3(512), 163840, 0, A, Bw, a_rows,
                          random, items, out);

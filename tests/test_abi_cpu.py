@@ -41,7 +41,7 @@ def test_stage_probe_library_loads():
     fn.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                    ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
     ms = ctypes.c_float(0.0)
-    assert fn(10, 4096, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1     # no such mode
+    assert fn(11, 4096, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1     # no such mode
     assert fn(3, 100, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1       # region under one tile
     assert fn(3, (1 << 20) + 1, 0, 0, 256, 16, 1, ctypes.byref(ms)) == -1
     assert fn(3, 4096, 0, 2, 256, 16, 1, ctypes.byref(ms)) == -1      # no such data kind
