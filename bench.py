@@ -350,6 +350,38 @@ def stage_probe(reps=20):
                           "frac_mfma_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}), flush=True)
 
 
+def mfma_ceiling(reps=10):
+    """Context for the bf16 rooflines, measured on this GPU with the
+    stage-loop probe on random bf16 operands: the fraction of the published
+    MFMA peak that the MFMA instructions alone sustain (the clock the chip
+    holds under that load), and that the wide engine's K-stage loop reaches
+    with its token rows gathered from a 128 MiB region, as the routed
+    gate/up GEMM reads them. None if the probe library is missing."""
+    import ctypes
+
+    path = os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "libmoe_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.moe_stage_probe.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_float)]
+    grid, items = 256, 16
+    flops = 2.0 * 256 * 256 * 512 * grid * items
+
+    def frac(mode, rows, rnd):
+        ms = ctypes.c_float(0.0)
+        rc = lib.moe_stage_probe(mode, rows, rnd, 1, grid, items, reps, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"moe_stage_probe(mode {mode}) returned {rc}")
+        return round(flops / (ms.value * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)
+
+    return {"mfma_only_frac": frac(7, 4096, 0),
+            "stage_loop_gathered_frac": frac(3, 131072, 1),
+            "source": "libmoe_probe.so stage-loop probe (bench.py --stage-probe modes 7 and 3), "
+                      "random bf16 operands, fractions of the published 2.5 PFLOP/s"}
+
+
 def pmc_summary(fetch_dir, write_dir, copyf_dir, copyw_dir, workload_name, out_path):
     """HBM bytes per launch of each kernel from rocprofv3 FETCH_SIZE and
     WRITE_SIZE runs (KiB per dispatch), each scaled by what the same counter
@@ -599,7 +631,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-pages", action="store_true",
-                    help="skip the pages' sampled timing (short runs under a profiler)")
+                    help="skip the pages' sampled timing and the MFMA ceiling probe (short runs "
+                         "under a profiler)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one forward step captured in a HIP graph")
     ap.add_argument("--maxtok", action="store_true",
@@ -769,6 +802,10 @@ def main():
                                  "unit": r["unit"], "bound": r["bound"]}
                              for k, r in rooflines.items()},
     }
+    # (skipped with --no-pages, the short runs under a profiler)
+    if p.dtype == "bf16" and not args.no_pages:
+        print("bench: MFMA ceiling probe", file=sys.stderr, flush=True)
+        line["mfma_ceiling"] = mfma_ceiling()
     if not args.no_train:
         print("bench: train step", file=sys.stderr, flush=True)
         line["train_step"] = train_step_line(B, max(5, args.steps // 5), 3, pages=not args.no_pages)
