@@ -408,13 +408,13 @@ hipError_t launch_route_dt(const void* x, const float* wr, int64_t T_, int d, in
     if (E <= 1) return launch_route_resident<T, 1, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 2) return launch_route_resident<T, 2, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 4) return launch_route_resident<T, 4, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
-    // fp32 rows are 2 KiB at d 512: one lane per token for all eight
-    // experts reads each row once instead of once per expert lane (4096
-    // tokens, E=8: 0.037 -> 0.027 ms); bf16 rows keep eight lanes a token
-    // (32768 tokens: 0.026 ms either way).
-    if (E <= 8 && sizeof(T) == 4)
-      return launch_route_resident<T, 1, 8, 1, 256>(x, wr, T_, d, E, k, idx, w, s);
-    if (E <= 8) return launch_route_resident<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
+    // One token per lane below 65536 tokens, so that more CUs get a
+    // workgroup (E=8: 4096 fp32 tokens 0.037 -> 0.021 ms, 32768 bf16
+    // tokens 0.026 -> 0.022 ms).
+    if (E <= 8) {
+      if (fits(8, 2)) return launch_route_resident<T, 8, 1, 2>(x, wr, T_, d, E, k, idx, w, s);
+      return launch_route_resident<T, 8, 1, 1>(x, wr, T_, d, E, k, idx, w, s);
+    }
     if (E <= 16) return launch_route_resident<T, 4, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
     if (E <= 32) {
       if (fits(8, 2)) return launch_route_resident<T, 8, 4, 2>(x, wr, T_, d, E, k, idx, w, s);
