@@ -130,6 +130,9 @@ ROUTE_LAYOUTS = [
     Problem(3000, 32, 4, 256, 64, 0, "bf16", 256),
     Problem(3000, 16, 4, 256, 64, 0, "bf16", 256),
     Problem(3000, 8, 2, 256, 64, 0, "bf16", 256),
+    Problem(3000, 8, 2, 128, 64, 0, "fp32", 256),
+    Problem(66000, 8, 2, 128, 64, 0, "bf16", 256),
+    Problem(66000, 8, 2, 128, 64, 0, "fp32", 256),
     Problem(3000, 4, 2, 256, 64, 0, "bf16", 256),
     Problem(3000, 2, 1, 256, 64, 0, "bf16", 256),
     Problem(3000, 64, 8, 768, 64, 0, "bf16", 256),
