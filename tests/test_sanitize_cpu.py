@@ -9,7 +9,7 @@
   validation and size queries, which return before anything reaches a
   device.
 
-A sanitizer report or a failed check makes the driver exit non-zero."""
+A sanitizer report or a failed check makes that program exit non-zero."""
 
 import concurrent.futures as cf
 import glob
