@@ -350,6 +350,30 @@ def stage_probe(reps=20):
                           "frac_mfma_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}), flush=True)
 
 
+STORE_PROBE_MODES = {0: "256x256 tiles, neighbouring workgroups share a row block",
+                     1: "128x512 tiles (whole rows)",
+                     2: "256x256 tiles, both column halves of a row block per workgroup"}
+
+
+def store_probe(reps=20):
+    """Write rate of the GEMM epilogue's store pattern (libmoe_probe.so):
+    1 GiB of bf16 [2^20][512] rows in three tile orders. One JSON line each."""
+    import ctypes
+
+    import torch
+
+    torch.cuda.set_device(0)
+    lib = ctypes.CDLL(os.path.join(ROOT, "dropless_grouped_gemm_router_amd", "libmoe_probe.so"))
+    lib.moe_store_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    for mode, what in STORE_PROBE_MODES.items():
+        ms = ctypes.c_float(0.0)
+        rc = lib.moe_store_probe(mode, reps, ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"moe_store_probe(mode {mode}) returned {rc}")
+        print(json.dumps({"store_probe": what, "mode": mode, "ms": round(ms.value, 4),
+                          "TB/s": round(2 ** 30 / (ms.value * 1e-3) / 1e12, 3)}), flush=True)
+
+
 def mfma_ceiling(reps=10):
     """Context for the bf16 rooflines, measured on this GPU with the
     stage-loop probe on random bf16 operands: the fraction of the published
@@ -645,6 +669,8 @@ def main():
     ap.add_argument("--reference", action="store_true",
                     help="only time reference rates on this GPU: a plain device copy and the "
                          "vendor BLAS (torch.matmul) on this layer's GEMM shapes")
+    ap.add_argument("--store-probe", action="store_true",
+                    help="write rate of the GEMM epilogues' store pattern in three tile orders")
     ap.add_argument("--stage-probe", action="store_true",
                     help="only run the stage-loop probe of the wide GEMM engine (libmoe_probe.so)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH", "WRITE", "COPYF", "COPYW"),
@@ -661,6 +687,9 @@ def main():
         return
     if args.stage_probe:
         stage_probe()
+        return
+    if args.store_probe:
+        store_probe()
         return
     if args.calibrate_copy:
         import torch

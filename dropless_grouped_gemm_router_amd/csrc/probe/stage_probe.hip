@@ -388,6 +388,41 @@ __global__ void probe_fill_kernel(uint32_t* p, int64_t n, int data) {
   }
 }
 
+// Store-pattern probe: 1 GiB of bf16 rows [2^20][512] written by 256
+// persistent workgroups of eight waves, each wave a 64 x 128 block as 16
+// stores of eight 128-byte row pieces (the engine's drain), in the order of
+// `mode`: 0 256 x 256 tiles, tile t = (row block t / 2, column half t % 2),
+// so neighbouring workgroups share a row block; 1 whole-row 128 x 512
+// tiles; 2 256 x 256 tiles with both column halves of a row block written
+// by one workgroup back to back.
+__device__ __forceinline__ void store_block(char* y, int64_t row0, int col0, int wr, int wc,
+                                            int lane, u32x4 v) {
+  for (int h = 0; h < 2; ++h)
+    for (int k = 0; k < 8; ++k) {
+      const int64_t r = row0 + wr + k * 8 + (lane >> 3);
+      *reinterpret_cast<u32x4*>(y + r * 1024 + col0 + wc + h * 128 + (lane & 7) * 16) = v;
+    }
+}
+
+__global__ __launch_bounds__(512) void store_probe_kernel(char* __restrict__ y, int mode) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = gridDim.x;
+  const u32x4 v = {1u + lane, 2u, 3u, 4u};
+  if (mode == 0) {
+    for (int t = blockIdx.x; t < 8192; t += G)
+      store_block(y, static_cast<int64_t>(t / 2) * 256, (t % 2) * 512, (wave / 2) * 64,
+                  (wave % 2) * 256, lane, v);
+  } else if (mode == 1) {
+    for (int t = blockIdx.x; t < 8192; t += G)
+      store_block(y, static_cast<int64_t>(t) * 128, 0, (wave / 4) * 64, (wave % 4) * 256, lane, v);
+  } else {
+    for (int b = blockIdx.x; b < 4096; b += G)
+      for (int half = 0; half < 2; ++half)
+        store_block(y, static_cast<int64_t>(b) * 256, half * 512, (wave / 2) * 64,
+                    (wave % 2) * 256, lane, v);
+  }
+}
+
 }  // namespace
 
 // Runs one probe configuration `reps` times after two warm-up launches and
@@ -452,5 +487,34 @@ PROBE_EXPORT int moe_stage_probe(int mode, int64_t a_rows, int random, int data,
   if (out) (void)hipFree(out);
   if (Bw) (void)hipFree(Bw);
   if (A) (void)hipFree(A);
+  return e == hipSuccess ? 0 : static_cast<int>(e);
+}
+
+// Runs the store-pattern probe `reps` times after two warm-up launches and
+// writes the average milliseconds per launch to *ms. Allocates and frees
+// its own 1 GiB buffer. Returns 0, -1 for a bad argument, or a HIP error.
+PROBE_EXPORT int moe_store_probe(int mode, int reps, float* ms) {
+  if (mode < 0 || mode > 2 || reps < 1 || !ms) return -1;
+  char* y = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  hipError_t e = hipMalloc(&y, size_t{1} << 30);
+  if (e == hipSuccess) e = hipEventCreate(&e0);
+  if (e == hipSuccess) e = hipEventCreate(&e1);
+  if (e == hipSuccess) {
+    for (int r = 0; r < 2; ++r)
+      hipLaunchKernelGGL(store_probe_kernel, dim3(256), dim3(512), 0, 0, y, mode);
+    e = hipEventRecord(e0, 0);
+    for (int r = 0; r < reps && e == hipSuccess; ++r)
+      hipLaunchKernelGGL(store_probe_kernel, dim3(256), dim3(512), 0, 0, y, mode);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e == hipSuccess) e = hipEventRecord(e1, 0);
+    if (e == hipSuccess) e = hipEventSynchronize(e1);
+    float t = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, e0, e1);
+    *ms = t / reps;
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (y) (void)hipFree(y);
   return e == hipSuccess ? 0 : static_cast<int>(e);
 }

@@ -47,6 +47,11 @@ def test_stage_probe_library_loads():
     assert fn(3, 4096, 0, 2, 256, 16, 1, ctypes.byref(ms)) == -1      # no such data kind
     assert fn(3, 4096, 0, 0, 0, 16, 1, ctypes.byref(ms)) == -1
     assert fn(3, 4096, 0, 0, 256, 16, 1, None) == -1
+    st = lib.moe_store_probe
+    st.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_float)]
+    assert st(3, 1, ctypes.byref(ms)) == -1      # no such store order
+    assert st(0, 0, ctypes.byref(ms)) == -1
+    assert st(0, 1, None) == -1
 
 
 def test_param_count_and_tiles():
